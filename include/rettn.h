@@ -1,0 +1,149 @@
+/*
+ * rettn.h -- C ABI of the Re-ttention static block-sparse attention library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method (Re-ttention: Ultra Sparse Visual Generation via Attention
+ * Statistical Reshape; summary page, section "Approach"; review thread,
+ * authors' replies to W1 of the first three reviews):
+ *   - a full-attention calibration step records, per (batch, head, query
+ *     token), rho = sparse-window softmax denominator / full denominator,
+ *     and the residual R = attention output of the masked (out-of-window)
+ *     keys normalised by the full denominator;
+ *   - each later sparse step attends only to the kept key blocks, rescales
+ *     the window-normalised output by the cached rho (ramped up by lambda)
+ *     and adds the cached R.
+ *
+ * Conventions shared by every entry point
+ *   - Q, K, V, O, R are [B, H, L, d] tensors in device memory with d
+ *     contiguous; element strides stride_b, stride_h, stride_l are given in
+ *     the descriptor and apply to all five.  rho is a contiguous float32
+ *     [B, H, L] device array.  The element type is the descriptor's dtype
+ *     (float32 or bfloat16); rho is always float32.
+ *   - The caller owns every buffer.  The library allocates no device
+ *     memory and keeps no state between calls besides its code objects.
+ *   - Launches are asynchronous on the given HIP stream (NULL = the null
+ *     stream); results are valid once the stream is ordered after them.
+ *   - Errors are returned as status codes; nothing throws or aborts.  All
+ *     arguments are validated before anything is launched; a rejected call
+ *     launches nothing and writes nothing.
+ *   - Outputs must not alias inputs.
+ */
+#ifndef RETTN_H
+#define RETTN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RETTN_OK = 0,
+    RETTN_EINVAL = 1,        /* a bad argument: null pointer, size, stride, alignment, mismatch */
+    RETTN_EUNSUPPORTED = 2,  /* a valid request outside what the kernels implement */
+    RETTN_EHIP = 3           /* a HIP runtime call or kernel launch failed */
+} rettn_status;
+
+typedef enum { RETTN_F32 = 0, RETTN_BF16 = 1 } rettn_dtype;
+
+/* Shape and layout of Q, K, V, O and R (all five share it).
+ *   B, H >= 1; L >= 1; 1 <= d <= 128; block in {32, 64, 128}.
+ *   bfloat16: d % 8 == 0 and every stride a multiple of 8 elements (16 bytes).
+ *   float32:  d % 4 == 0 and every stride a multiple of 4 elements (16 bytes).
+ *   Every row must fit: stride_l >= d. */
+typedef struct {
+    int32_t B, H, L, d, block;
+    int32_t dtype;                      /* rettn_dtype */
+    int64_t stride_b, stride_h, stride_l;
+} rettn_desc;
+
+/* Static block-mask generators (the mask is the same at every denoising
+ * step: summary page, "Limitations"; review thread, reply to W2 of the
+ * first review).  The pages print no geometry; these are the readings used:
+ *   RETTN_MASK_DIAG        query block qb keeps key block qb.
+ *   RETTN_MASK_BAND        keeps w consecutive key blocks starting at
+ *                          clamp(qb - (w-1)/2, 0, nb - w)  (1 <= w <= nb).
+ *   RETTN_MASK_COGVIDEO3D  keeps text blocks [0, text_blocks) and the blocks
+ *                          {qb-1, qb, qb+1, qb-tshift, qb+tshift} inside [0, nb).
+ *   RETTN_MASK_FULL        keeps every block (0% sparsity). */
+typedef enum {
+    RETTN_MASK_DIAG = 0,
+    RETTN_MASK_BAND = 1,
+    RETTN_MASK_COGVIDEO3D = 2,
+    RETTN_MASK_FULL = 3
+} rettn_mask_kind;
+
+typedef struct {
+    int32_t kind;          /* rettn_mask_kind */
+    int32_t nb;            /* blocks per side, >= 1 */
+    int32_t w;             /* BAND width */
+    int32_t text_blocks;   /* COGVIDEO3D: leading text blocks, >= 0 */
+    int32_t tshift;        /* COGVIDEO3D: temporal offset in blocks, >= 1 */
+} rettn_mask_spec;
+
+/* The compacted static mask, all arrays in device memory and owned by the caller.
+ *   mask     uint8 [nqb * nkb] row-major; nonzero = key block kept.
+ *   row_ptr  int32 [nqb + 1]; col_idx int32 [nnz], ascending within a row. */
+typedef struct {
+    int32_t nqb, nkb, nnz;
+    const int32_t* row_ptr;
+    const int32_t* col_idx;
+    const uint8_t* mask;
+} rettn_index;
+
+/* Build a static block mask on the host.
+ * mask_host: caller-owned host buffer of spec->nb * spec->nb bytes, filled
+ * with 0/1.  Returns RETTN_EINVAL for a null pointer, nb < 1 or nb > 65536,
+ * an unknown kind, or generator parameters out of range. */
+rettn_status rettn_mask_build(const rettn_mask_spec* spec, uint8_t* mask_host);
+
+/* Compact a device block mask into its CSR block index (kept key blocks of
+ * each query block, ascending).
+ *   mask_dev    uint8 [nqb * nkb], device.
+ *   row_ptr_dev int32 [nqb + 1], device, written.
+ *   col_idx_dev int32 capacity nqb * nkb, device; the first nnz entries are written.
+ *   nnz_host    host int32, written with the number of kept pairs.
+ * The one call in the library that synchronises: it waits on `stream` to
+ * read nnz back.  The result is unique, so it is bit-exact by construction. */
+rettn_status rettn_index_build(const uint8_t* mask_dev, int32_t nqb, int32_t nkb,
+                               int32_t* row_ptr_dev, int32_t* col_idx_dev,
+                               int32_t* nnz_host, hipStream_t stream);
+
+/* Full-attention calibration step.  For each (b, h) and query row i < L,
+ * over every key j < L, with s_j = <q_i, k_j> / sqrt(d) and W(i) the kept keys:
+ *   O_i   = softmax(s) V                                  (full attention)
+ *   rho_i = sum_{j in W(i)} e^{s_j} / sum_j e^{s_j}
+ *   R_i   = sum_{j not in W(i)} e^{s_j} v_j / sum_j e^{s_j}
+ * (review thread, replies to W1 of the first and second reviews: rho is the
+ * denominator ratio, R holds only the masked tokens' attention; answer to Q2
+ * of the first review: both per head and per token).
+ * Writes O and R (dtype, descriptor layout) and rho (float32 [B,H,L]).
+ * idx must describe a mask of ceil(L/block) x ceil(L/block) blocks (only
+ * idx->mask is read).  For bfloat16, the P*V products run with P and V in
+ * float16 (V converted exactly for |V| <= 65504); V beyond that range
+ * overflows to infinity in O and R. */
+rettn_status rettn_calibrate(const rettn_desc* desc, const void* Q, const void* K, const void* V,
+                             const rettn_index* idx, void* O, float* rho, void* R,
+                             hipStream_t stream);
+
+/* Sparse step `step` (>= 1 sparse steps since the last calibration):
+ *   O'_i = min(1, rho_i (1 + lambda step)) * softmax_{W(i)}(s') V'_{W(i)} + R_i
+ * over the kept key blocks only (review thread, replies to W1 of the first
+ * and third reviews; the ramp-up lambda: answer to W1 of the fourth review;
+ * the pages print no ramp formula: this multiplicative, clamped ramp is the
+ * reading used).  A row with no kept block gets O'_i = R_i.  Reads rho and R
+ * cached by rettn_calibrate; idx->row_ptr and idx->col_idx are walked.
+ * lambda must be finite and >= 0. */
+rettn_status rettn_sparse(const rettn_desc* desc, const void* Q, const void* K, const void* V,
+                          const rettn_index* idx, const float* rho, const void* R,
+                          float lambda, int32_t step, void* O, hipStream_t stream);
+
+/* A static string naming a status code. */
+const char* rettn_status_str(rettn_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RETTN_H */

@@ -1,0 +1,212 @@
+"""Re-ttention attention steps in float64 -- oracle side.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Sources (the pages describe the method in prose and by one worked example):
+  * Re-ttention summary page, "Approach": a full-attention step caches the
+    ratio of the sparse to the full softmax denominator; later steps rescale
+    the sparse attention probabilities by it (with a ramp-up) and add a
+    cached residual equal to the masked tokens' attention output.
+  * Re-ttention review thread, authors' replies to W1 (first review), W1
+    (second review) and W1 (third review): the worked example
+    [0.1, 0.4, 0.4, 0.1] with a middle-two window, rho = 0.8, residual
+    [0.1, 0, 0, 0.1], drifted row [0.1, 0.3, 0.5, 0.1] rebuilt exactly; the
+    residual holds only the masked tokens' attention.
+  * Review thread, answer to Q2 (first review): rho is per head and per
+    token, never averaged.
+  * Review thread, answer to W1 (fourth review): attention drifts local over
+    the denoising steps, so rho grows; the ramp-up lambda corrects for it.
+  * Review thread, answers to Q3 (first review) and W2 (fourth review): a
+    full-attention step every T steps resets the cache.
+
+Readings where the pages are silent (each is listed in the design notes):
+  * rho = D_window / D_full per (batch, head, query token).  The defining
+    equation is referenced but not printed; this reading reproduces 0.8 in
+    the worked example and grows when attention turns local.
+  * The ramp: rho~ = min(1, rho * (1 + lambda * k)), k = sparse steps since
+    the last calibration (k >= 1).  PARITY UNPINNED by the pages beyond
+    lambda = 0 (no formula is printed); pinned only by internal algebra.
+  * Softmax scale tau = 1/sqrt(d) with the true head dimension.
+  * Keys at positions >= L do not exist; an empty window gives O' = R.
+"""
+import math
+
+import numpy as np
+
+
+def tau(d):
+    return 1.0 / math.sqrt(d)
+
+
+def ramp(rho, lam, step):
+    """Ramped ratio used at sparse step `step` (>= 1) after a calibration."""
+    rho = np.asarray(rho, dtype=np.float64)
+    return np.minimum(1.0, rho * (1.0 + float(lam) * float(step)))
+
+
+def key_keep(mask, block, L, qb):
+    """Token-level kept keys of query block qb: key j is kept iff mask[qb, j // block] != 0."""
+    blocks = np.arange(L) // block
+    return np.asarray(mask)[qb, blocks] != 0
+
+
+def _rows_by_block(rows, block):
+    rows = np.asarray(rows, dtype=np.int64)
+    out = {}
+    for pos, i in enumerate(rows):
+        out.setdefault(int(i) // block, []).append(pos)
+    return out
+
+
+def _as64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def calibrate(q, k, v, mask, block, rows=None):
+    """Full-attention calibration step.
+
+    For each (b, h) and query row i, over all keys j < L:
+        s_j = tau <q_i, k_j>,  m = max_j s_j,  e_j = exp(s_j - m)
+        D = sum_j e_j,  D_in = sum_{j in W(i)} e_j
+        O_i   = sum_j e_j v_j / D                 (full softmax attention)
+        rho_i = D_in / D
+        R_i   = sum_{j not in W(i)} e_j v_j / D   (masked tokens only, full denominator)
+    Returns O [B,H,n,d], rho [B,H,n], R [B,H,n,d] for the requested rows.
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, H, L, d = q.shape
+    rows = np.arange(L) if rows is None else np.asarray(rows, dtype=np.int64)
+    n = len(rows)
+    o = np.zeros((B, H, n, d))
+    r = np.zeros((B, H, n, d))
+    rho = np.zeros((B, H, n))
+    t = tau(d)
+    groups = _rows_by_block(rows, block)
+    for b in range(B):
+        for h in range(H):
+            for qb, pos in groups.items():
+                keep = key_keep(mask, block, L, qb)
+                qi = q[b, h, rows[pos]]
+                s = t * (qi @ k[b, h].T)
+                m = s.max(axis=1, keepdims=True)
+                e = np.exp(s - m)
+                D = e.sum(axis=1)
+                D_in = e[:, keep].sum(axis=1)
+                o[b, h, pos] = (e @ v[b, h]) / D[:, None]
+                r[b, h, pos] = (e[:, ~keep] @ v[b, h][~keep]) / D[:, None]
+                rho[b, h, pos] = D_in / D
+    return o, rho, r
+
+
+def window_attention(q, k, v, mask, block, rows=None):
+    """Plain sparse attention: softmax over the kept keys only (pre-softmax masking).
+
+    Rows whose window is empty give zeros.  Also returns the window mass D'
+    is not needed by callers; only the normalised output is returned.
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, H, L, d = q.shape
+    rows = np.arange(L) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.zeros((B, H, len(rows), d))
+    t = tau(d)
+    groups = _rows_by_block(rows, block)
+    for b in range(B):
+        for h in range(H):
+            for qb, pos in groups.items():
+                keep = key_keep(mask, block, L, qb)
+                if not keep.any():
+                    continue
+                kk, vv = k[b, h][keep], v[b, h][keep]
+                s = t * (q[b, h, rows[pos]] @ kk.T)
+                m = s.max(axis=1, keepdims=True)
+                e = np.exp(s - m)
+                out[b, h, pos] = (e @ vv) / e.sum(axis=1)[:, None]
+    return out
+
+
+def sparse_step(q, k, v, mask, block, rho, r, lam, step, rows=None):
+    """Sparse step k after a calibration (Re-ttention's statistical reshape).
+
+    Over the kept keys W(i) only:
+        s'_j = tau <q'_i, k'_j>, m' = max_W s', e'_j = exp(s'_j - m'), D' = sum_W e'
+        O'_i = min(1, rho_i (1 + lambda k)) * sum_W e'_j v'_j / D' + R_i
+    and O'_i = R_i when W(i) is empty.  `rho` [B,H,n] and `r` [B,H,n,d] are
+    the cached values for the requested rows, in the same order.
+    """
+    o_sp = window_attention(q, k, v, mask, block, rows)
+    rho = _as64(rho)
+    r = _as64(r)
+    L = np.asarray(q).shape[2]
+    rows_arr = np.arange(L) if rows is None else np.asarray(rows, dtype=np.int64)
+    nonempty = np.array([bool(np.asarray(mask)[int(i) // block].any()) for i in rows_arr])
+    scale = ramp(rho, lam, step) * nonempty[None, None, :]
+    return scale[..., None] * o_sp + r
+
+
+def full_attention(q, k, v, rows=None):
+    """softmax(tau Q K^T) V for the requested rows (dense reference)."""
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, H, L, d = q.shape
+    rows = np.arange(L) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.zeros((B, H, len(rows), d))
+    t = tau(d)
+    for b in range(B):
+        for h in range(H):
+            s = t * (q[b, h, rows] @ k[b, h].T)
+            e = np.exp(s - s.max(axis=1, keepdims=True))
+            out[b, h] = (e @ v[b, h]) / e.sum(axis=1)[:, None]
+    return out
+
+
+def textbook_attention(q, k, v):
+    """softmax(tau Q K^T) V with explicit Python loops and math.exp (tiny inputs only)."""
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, H, L, d = q.shape
+    t = tau(d)
+    out = np.zeros((B, H, L, d))
+    for b in range(B):
+        for h in range(H):
+            for i in range(L):
+                scores = []
+                for j in range(L):
+                    acc = 0.0
+                    for c in range(d):
+                        acc += q[b, h, i, c] * k[b, h, j, c]
+                    scores.append(t * acc)
+                big = max(scores)
+                w = [math.exp(sc - big) for sc in scores]
+                tot = sum(w)
+                for c in range(d):
+                    out[b, h, i, c] = sum(w[j] * v[b, h, j, c] for j in range(L)) / tot
+    return out
+
+
+def ditfastattn_residual(o_full, o_window):
+    """DiTFastAttn's cached residual: full minus window attention at the calibration step
+    (review thread, reply to W1 of the first review).  Comparator only."""
+    return _as64(o_full) - _as64(o_window)
+
+
+def ditfastattn_step(q, k, v, mask, block, r_dfa, rows=None):
+    """DiTFastAttn's reconstruction at a later step: window attention plus the cached difference."""
+    return window_attention(q, k, v, mask, block, rows) + _as64(r_dfa)
+
+
+def post_softmax_masked(q, k, v, mask, block, rows=None):
+    """Post-softmax masking: full-softmax probabilities of the kept keys only, full denominator
+    kept (summary page, "Surprising findings").  At a calibration step this equals rho * O_window."""
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, H, L, d = q.shape
+    rows = np.arange(L) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.zeros((B, H, len(rows), d))
+    t = tau(d)
+    groups = _rows_by_block(rows, block)
+    for b in range(B):
+        for h in range(H):
+            for qb, pos in groups.items():
+                keep = key_keep(mask, block, L, qb)
+                s = t * (q[b, h, rows[pos]] @ k[b, h].T)
+                e = np.exp(s - s.max(axis=1, keepdims=True))
+                p = e / e.sum(axis=1, keepdims=True)
+                out[b, h, pos] = p[:, keep] @ v[b, h][keep]
+    return out
