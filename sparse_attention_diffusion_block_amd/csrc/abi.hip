@@ -1,0 +1,180 @@
+// C ABI of librettn: argument validation, the host-side static mask
+// generators and dispatch to the gfx950 kernels.  Every argument is checked
+// before anything is launched; a rejected call launches nothing.
+#include <math.h>
+#include <string.h>
+
+#include <initializer_list>
+
+#include "../../include/rettn.h"
+#include "attn.h"
+
+namespace {
+
+using rettn::AttnArgs;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Shape, dtype, stride and pointer checks common to both attention steps.
+rettn_status check_desc(const rettn_desc* d, const rettn_index* idx) {
+    if (!d || !idx) return RETTN_EINVAL;
+    if (d->B < 1 || d->H < 1 || d->L < 1) return RETTN_EINVAL;
+    if (d->d < 1 || d->d > 128) return RETTN_EINVAL;
+    if (d->block != 32 && d->block != 64 && d->block != 128) return RETTN_EINVAL;
+    if (d->dtype != RETTN_F32 && d->dtype != RETTN_BF16) return RETTN_EINVAL;
+    const int64_t gran = d->dtype == RETTN_BF16 ? 8 : 4;   // elements per 16 bytes
+    if (d->d % gran != 0) return RETTN_EINVAL;
+    if (d->stride_l < d->d || d->stride_h < 1 || d->stride_b < 1) return RETTN_EINVAL;
+    if (d->stride_l % gran || d->stride_h % gran || d->stride_b % gran) return RETTN_EINVAL;
+    const int64_t nb = cdiv(d->L, d->block);
+    if (idx->nqb != nb || idx->nkb != nb) return RETTN_EINVAL;
+    if ((int64_t)d->B * d->H * nb > 0x7fffffff) return RETTN_EUNSUPPORTED;
+    if ((int64_t)d->B * d->H * d->L > ((int64_t)1 << 40)) return RETTN_EUNSUPPORTED;
+    return RETTN_OK;
+}
+
+// Tensors are read and written in 16-byte chunks; rho and the index arrays element-wise.
+rettn_status check_tensors(std::initializer_list<const void*> ps) {
+    for (const void* p : ps)
+        if (!p || !aligned16(p)) return RETTN_EINVAL;
+    return RETTN_OK;
+}
+
+rettn_status check_words(std::initializer_list<const void*> ps) {
+    for (const void* p : ps)
+        if (!p || ((uintptr_t)p & 3u) != 0) return RETTN_EINVAL;
+    return RETTN_OK;
+}
+
+AttnArgs make_args(const rettn_desc* d, const void* Q, const void* K, const void* V, const rettn_index* idx, void* O) {
+    AttnArgs a{};
+    a.Q = Q;
+    a.K = K;
+    a.V = V;
+    a.O = O;
+    a.row_ptr = idx->row_ptr;
+    a.col_idx = idx->col_idx;
+    a.mask = idx->mask;
+    a.sb = d->stride_b;
+    a.sh = d->stride_h;
+    a.sl = d->stride_l;
+    a.B = d->B;
+    a.H = d->H;
+    a.L = d->L;
+    a.d = d->d;
+    a.nqb = idx->nqb;
+    a.nkb = idx->nkb;
+    a.c = (float)(1.4426950408889634 / sqrt((double)d->d));
+    a.ramp = 1.f;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rettn_status_str(rettn_status s) {
+    switch (s) {
+        case RETTN_OK: return "RETTN_OK";
+        case RETTN_EINVAL: return "RETTN_EINVAL: invalid argument";
+        case RETTN_EUNSUPPORTED: return "RETTN_EUNSUPPORTED: outside the implemented shapes";
+        case RETTN_EHIP: return "RETTN_EHIP: HIP runtime or launch failure";
+    }
+    return "unknown rettn_status";
+}
+
+rettn_status rettn_mask_build(const rettn_mask_spec* spec, uint8_t* mask) {
+    if (!spec || !mask) return RETTN_EINVAL;
+    const int nb = spec->nb;
+    if (nb < 1 || nb > 65536) return RETTN_EINVAL;
+    switch (spec->kind) {
+        case RETTN_MASK_DIAG:
+        case RETTN_MASK_FULL: break;
+        case RETTN_MASK_BAND:
+            if (spec->w < 1 || spec->w > nb) return RETTN_EINVAL;
+            break;
+        case RETTN_MASK_COGVIDEO3D:
+            if (spec->text_blocks < 0 || spec->text_blocks > nb || spec->tshift < 1) return RETTN_EINVAL;
+            break;
+        default: return RETTN_EINVAL;
+    }
+    memset(mask, 0, (size_t)nb * (size_t)nb);
+    for (int qb = 0; qb < nb; ++qb) {
+        uint8_t* row = mask + (size_t)qb * nb;
+        switch (spec->kind) {
+            case RETTN_MASK_DIAG: row[qb] = 1; break;
+            case RETTN_MASK_FULL: memset(row, 1, (size_t)nb); break;
+            case RETTN_MASK_BAND: {
+                int lo = qb - (spec->w - 1) / 2;
+                if (lo > nb - spec->w) lo = nb - spec->w;
+                if (lo < 0) lo = 0;
+                memset(row + lo, 1, (size_t)spec->w);
+                break;
+            }
+            case RETTN_MASK_COGVIDEO3D: {
+                memset(row, 1, (size_t)spec->text_blocks);
+                const int nbr[5] = {qb - 1, qb, qb + 1, qb - spec->tshift, qb + spec->tshift};
+                for (int k : nbr)
+                    if (k >= 0 && k < nb) row[k] = 1;
+                break;
+            }
+        }
+    }
+    return RETTN_OK;
+}
+
+rettn_status rettn_index_build(const uint8_t* mask_dev, int32_t nqb, int32_t nkb, int32_t* row_ptr_dev,
+                               int32_t* col_idx_dev, int32_t* nnz_host, hipStream_t stream) {
+    if (!mask_dev || !row_ptr_dev || !col_idx_dev || !nnz_host) return RETTN_EINVAL;
+    if (nqb < 1 || nkb < 1 || (int64_t)nqb * nkb > 0x7fffffff) return RETTN_EINVAL;
+    if (rettn::launch_index_build(mask_dev, nqb, nkb, row_ptr_dev, col_idx_dev, stream) != hipSuccess)
+        return RETTN_EHIP;
+    int32_t nnz = 0;
+    if (hipMemcpyAsync(&nnz, row_ptr_dev + nqb, sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess)
+        return RETTN_EHIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return RETTN_EHIP;
+    *nnz_host = nnz;
+    return RETTN_OK;
+}
+
+rettn_status rettn_calibrate(const rettn_desc* desc, const void* Q, const void* K, const void* V,
+                             const rettn_index* idx, void* O, float* rho, void* R, hipStream_t stream) {
+    rettn_status st = check_desc(desc, idx);
+    if (st != RETTN_OK) return st;
+    st = check_tensors({Q, K, V, O, R});
+    if (st != RETTN_OK) return st;
+    st = check_words({rho});
+    if (st != RETTN_OK) return st;
+    if (!idx->mask) return RETTN_EINVAL;
+    AttnArgs a = make_args(desc, Q, K, V, idx, O);
+    a.R_out = R;
+    a.rho_out = rho;
+    const hipError_t e = desc->dtype == RETTN_BF16 ? rettn::launch_calibrate_bf16(a, desc->block, stream)
+                                                   : rettn::launch_calibrate_f32(a, desc->block, stream);
+    return e == hipSuccess ? RETTN_OK : RETTN_EHIP;
+}
+
+rettn_status rettn_sparse(const rettn_desc* desc, const void* Q, const void* K, const void* V,
+                          const rettn_index* idx, const float* rho, const void* R, float lambda, int32_t step,
+                          void* O, hipStream_t stream) {
+    rettn_status st = check_desc(desc, idx);
+    if (st != RETTN_OK) return st;
+    st = check_tensors({Q, K, V, O, R});
+    if (st != RETTN_OK) return st;
+    st = check_words({rho, idx->row_ptr});
+    if (st != RETTN_OK) return st;
+    if (idx->nnz > 0 && check_words({idx->col_idx}) != RETTN_OK) return RETTN_EINVAL;
+    if (!(lambda >= 0.f) || !isfinite(lambda) || step < 0) return RETTN_EINVAL;
+    if (idx->nnz < 0 || (int64_t)idx->nnz > (int64_t)idx->nqb * idx->nkb) return RETTN_EINVAL;
+    AttnArgs a = make_args(desc, Q, K, V, idx, O);
+    a.R_in = R;
+    a.rho_in = rho;
+    a.ramp = (float)(1.0 + (double)lambda * (double)step);
+    const hipError_t e = desc->dtype == RETTN_BF16 ? rettn::launch_sparse_bf16(a, desc->block, stream)
+                                                   : rettn::launch_sparse_f32(a, desc->block, stream);
+    return e == hipSuccess ? RETTN_OK : RETTN_EHIP;
+}
+
+}  // extern "C"

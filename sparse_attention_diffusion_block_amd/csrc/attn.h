@@ -1,0 +1,41 @@
+// Kernel-side argument block and launchers of the attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rettn {
+
+struct AttnArgs {
+    const void* Q;
+    const void* K;
+    const void* V;
+    void* O;
+    // calibration writes R and rho; the sparse step reads them
+    void* R_out;
+    float* rho_out;
+    const void* R_in;
+    const float* rho_in;
+    const int32_t* row_ptr;
+    const int32_t* col_idx;
+    const uint8_t* mask;
+    int64_t sb, sh, sl;       // element strides of Q, K, V, O, R
+    int32_t B, H, L, d;
+    int32_t nqb, nkb;
+    float c;                  // log2(e) / sqrt(d): scores enter exp2 pre-scaled
+    float ramp;               // 1 + lambda * step (sparse step only)
+    int32_t G;                // work-groups in the launch
+};
+
+// d is padded to DP in {32, 64, 96, 128} inside the kernels.
+inline int pad_d(int d) { return d <= 32 ? 32 : d <= 64 ? 64 : d <= 96 ? 96 : 128; }
+
+hipError_t launch_calibrate_bf16(AttnArgs a, int block, hipStream_t s);
+hipError_t launch_sparse_bf16(AttnArgs a, int block, hipStream_t s);
+hipError_t launch_calibrate_f32(AttnArgs a, int block, hipStream_t s);
+hipError_t launch_sparse_f32(AttnArgs a, int block, hipStream_t s);
+
+hipError_t launch_index_build(const uint8_t* mask, int nqb, int nkb, int32_t* row_ptr, int32_t* col_idx,
+                              hipStream_t s);
+
+}  // namespace rettn

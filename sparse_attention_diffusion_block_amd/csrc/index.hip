@@ -1,0 +1,84 @@
+// Block-index compactor: the static block mask M [nqb, nkb] (uint8, nonzero
+// = kept) becomes its CSR list of kept key blocks per query block, ascending.
+// The mask is fixed for the whole denoising run (Re-ttention summary page,
+// "Limitations"; review thread, reply to W2 of the first review), so this
+// runs once per mask.  Three launches:
+//   1. one wave per query block counts its kept blocks into row_ptr[qb + 1];
+//   2. one work-group turns the counts into offsets (inclusive scan);
+//   3. one wave per query block writes its kept block ids in ascending order,
+//      64 at a time: a ballot over the chunk and each lane's rank in it
+//      (mbcnt) give every kept id its slot.
+// The result is unique, so it is reproduced bit-exactly.
+#include "attn.h"
+#include "common.h"
+
+namespace rettn {
+
+__global__ void __launch_bounds__(64) index_count_kernel(const uint8_t* __restrict__ mask, int nkb,
+                                                         int32_t* __restrict__ row_ptr) {
+    const int qb = blockIdx.x;
+    const uint8_t* mrow = mask + (int64_t)qb * nkb;
+    int cnt = 0;
+    for (int kb = threadIdx.x; kb < nkb; kb += 64) cnt += mrow[kb] != 0;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+    if (threadIdx.x == 0) {
+        row_ptr[qb + 1] = cnt;
+        if (qb == 0) row_ptr[0] = 0;
+    }
+}
+
+__global__ void __launch_bounds__(1024) index_scan_kernel(int32_t* __restrict__ row_ptr, int nqb) {
+    __shared__ int32_t part[1024];
+    __shared__ int32_t carry;
+    const int t = threadIdx.x;
+    if (t == 0) carry = 0;
+    __syncthreads();
+    for (int start = 1; start <= nqb; start += 1024) {
+        const int i = start + t;
+        int v = i <= nqb ? row_ptr[i] : 0;
+        part[t] = v;
+        __syncthreads();
+        // Hillis-Steele inclusive scan over the 1024-entry chunk
+        for (int off = 1; off < 1024; off <<= 1) {
+            const int add = t >= off ? part[t - off] : 0;
+            __syncthreads();
+            part[t] += add;
+            __syncthreads();
+        }
+        if (i <= nqb) row_ptr[i] = part[t] + carry;
+        __syncthreads();
+        if (t == 1023) carry += part[1023];
+        __syncthreads();
+    }
+}
+
+__global__ void __launch_bounds__(64) index_scatter_kernel(const uint8_t* __restrict__ mask, int nkb,
+                                                           const int32_t* __restrict__ row_ptr,
+                                                           int32_t* __restrict__ col_idx) {
+    const int qb = blockIdx.x;
+    const uint8_t* mrow = mask + (int64_t)qb * nkb;
+    int out = row_ptr[qb];
+    for (int kb0 = 0; kb0 < nkb; kb0 += 64) {
+        const int kb = kb0 + (int)threadIdx.x;
+        const bool keep = kb < nkb && mrow[kb] != 0;
+        const uint64_t bal = __ballot(keep);
+        const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+        if (keep) col_idx[out + rank] = kb;
+        out += __popcll(bal);
+    }
+}
+
+hipError_t launch_index_build(const uint8_t* mask, int nqb, int nkb, int32_t* row_ptr, int32_t* col_idx,
+                              hipStream_t s) {
+    hipLaunchKernelGGL(index_count_kernel, dim3(nqb), dim3(64), 0, s, mask, nkb, row_ptr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(index_scan_kernel, dim3(1), dim3(1024), 0, s, row_ptr, nqb);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(index_scatter_kernel, dim3(nqb), dim3(64), 0, s, mask, nkb, (const int32_t*)row_ptr, col_idx);
+    return hipGetLastError();
+}
+
+}  // namespace rettn

@@ -1,0 +1,170 @@
+"""Python binding of librettn (include/rettn.h): argument marshalling only.
+
+PyTorch supplies device memory and the current HIP stream; every step of the
+path runs in the library's gfx950 kernels.  There is no fallback: if the
+library is not built, or a call is rejected, an exception is raised.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librettn.so")
+
+RETTN_F32, RETTN_BF16 = 0, 1
+MASK_DIAG, MASK_BAND, MASK_COGVIDEO3D, MASK_FULL = 0, 1, 2, 3
+EXPORTED = ("rettn_mask_build", "rettn_index_build", "rettn_calibrate", "rettn_sparse", "rettn_status_str")
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("block", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64), ("stride_l", ctypes.c_int64)]
+
+
+class MaskSpec(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("nb", ctypes.c_int32), ("w", ctypes.c_int32),
+                ("text_blocks", ctypes.c_int32), ("tshift", ctypes.c_int32)]
+
+
+class Index(ctypes.Structure):
+    _fields_ = [("nqb", ctypes.c_int32), ("nkb", ctypes.c_int32), ("nnz", ctypes.c_int32),
+                ("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p), ("mask", ctypes.c_void_p)]
+
+
+class RettnError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {lib().rettn_status_str(status).decode()}")
+
+
+_lib = None
+
+
+def lib():
+    """Load librettn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run sparse_attention_diffusion_block_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int32
+        L.rettn_status_str.argtypes = [ctypes.c_int]
+        L.rettn_status_str.restype = ctypes.c_char_p
+        L.rettn_mask_build.argtypes = [ctypes.POINTER(MaskSpec), vp]
+        L.rettn_mask_build.restype = ctypes.c_int
+        L.rettn_index_build.argtypes = [vp, i32, i32, vp, vp, ctypes.POINTER(i32), vp]
+        L.rettn_index_build.restype = ctypes.c_int
+        L.rettn_calibrate.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, ctypes.POINTER(Index), vp, vp, vp, vp]
+        L.rettn_calibrate.restype = ctypes.c_int
+        L.rettn_sparse.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, ctypes.POINTER(Index), vp, vp,
+                                   ctypes.c_float, i32, vp, vp]
+        L.rettn_sparse.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status, what):
+    if status != 0:
+        raise RettnError(status, what)
+
+
+def mask_build(kind, nb, w=0, text_blocks=0, tshift=0):
+    """Static block mask [nb, nb] (uint8 0/1) built by the library on the host."""
+    out = np.zeros((nb, nb), dtype=np.uint8)
+    spec = MaskSpec(kind, nb, w, text_blocks, tshift)
+    _check(lib().rettn_mask_build(ctypes.byref(spec), out.ctypes.data_as(ctypes.c_void_p)), "rettn_mask_build")
+    return out
+
+
+class BlockIndex:
+    """A static block mask on the device and its CSR index (kept key blocks per query block)."""
+
+    def __init__(self, mask, row_ptr, col_idx, nnz, block):
+        self.mask, self.row_ptr, self.col_idx, self.nnz, self.block = mask, row_ptr, col_idx, nnz, block
+        self.nqb, self.nkb = mask.shape
+
+    def c_struct(self):
+        return Index(self.nqb, self.nkb, self.nnz, self.row_ptr.data_ptr(), self.col_idx.data_ptr(),
+                     self.mask.data_ptr())
+
+
+def _stream(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def index_build(mask, block):
+    """Compact a [nqb, nkb] uint8 mask (host array or device tensor) on the GPU; synchronises once."""
+    import torch
+    m = torch.as_tensor(np.asarray(mask) if not isinstance(mask, torch.Tensor) else mask)
+    m = m.to(device="cuda", dtype=torch.uint8).contiguous()
+    nqb, nkb = m.shape
+    row_ptr = torch.empty(nqb + 1, dtype=torch.int32, device=m.device)
+    col_idx = torch.empty(max(nqb * nkb, 1), dtype=torch.int32, device=m.device)
+    nnz = ctypes.c_int32(0)
+    _check(lib().rettn_index_build(m.data_ptr(), nqb, nkb, row_ptr.data_ptr(), col_idx.data_ptr(),
+                                   ctypes.byref(nnz), _stream(m.device)), "rettn_index_build")
+    return BlockIndex(m, row_ptr, col_idx, nnz.value, block)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return RETTN_BF16
+    if t.dtype == torch.float32:
+        return RETTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16")
+
+
+def _prep(tensors):
+    """Tensors sharing one [B,H,L,d] layout with d contiguous (copied to contiguous otherwise)."""
+    ts = list(tensors)
+    for t in ts:
+        if not t.is_cuda or t.dim() != 4:
+            raise ValueError("expected CUDA tensors of shape [B, H, L, d]")
+        if t.shape != ts[0].shape or t.dtype != ts[0].dtype:
+            raise ValueError("Q, K, V (and R) must share shape and dtype")
+    if any(t.stride() != ts[0].stride() for t in ts) or ts[0].stride(3) != 1:
+        ts = [t.contiguous() for t in ts]
+    return ts
+
+
+def _desc(t, block):
+    B, H, L, d = t.shape
+    sb, sh, sl, _ = t.stride()
+    return Desc(B, H, L, d, block, _dtype_code(t), sb, sh, sl)
+
+
+def calibrate(q, k, v, index, out=None):
+    """Full-attention calibration step -> (O, rho, R).  O and R have q's dtype; rho is float32 [B,H,L]."""
+    import torch
+    q, k, v = _prep((q, k, v))
+    B, H, L, d = q.shape
+    if out is None:
+        o = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+        r = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+        rho = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    else:
+        o, rho, r = out
+    desc = _desc(q, index.block)
+    idx = index.c_struct()
+    _check(lib().rettn_calibrate(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(idx),
+                                 o.data_ptr(), rho.data_ptr(), r.data_ptr(), _stream(q.device)), "rettn_calibrate")
+    return o, rho, r
+
+
+def sparse(q, k, v, index, rho, r, lam=0.04, step=1, out=None):
+    """Sparse step `step` after a calibration: min(1, rho (1 + lam step)) * window attention + R."""
+    import torch
+    q, k, v, r = _prep((q, k, v, r))
+    if rho.dtype != torch.float32 or not rho.is_contiguous() or tuple(rho.shape) != tuple(q.shape[:3]):
+        raise ValueError("rho must be a contiguous float32 [B, H, L] tensor")
+    o = out if out is not None else torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    desc = _desc(q, index.block)
+    idx = index.c_struct()
+    _check(lib().rettn_sparse(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(idx),
+                              rho.data_ptr(), r.data_ptr(), float(lam), int(step), o.data_ptr(), _stream(q.device)),
+           "rettn_sparse")
+    return o

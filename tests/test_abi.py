@@ -1,0 +1,131 @@
+"""The C ABI library on the CPU: it loads, exports every symbol include/rettn.h
+declares, builds masks bit-identical to the oracle's independent generators,
+and rejects bad arguments before launching anything (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import sparse_attention_diffusion_block_amd as rt
+from sparse_attention_diffusion_block_amd import rettn as b
+from oracle import masks as om
+from workloads import CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+EINVAL = 1
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "rettn.h")).read()
+    return sorted(set(re.findall(r"\b(rettn_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_symbols()
+    assert set(names) == set(rt.EXPORTED)
+    lib = rt.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = rt.lib()
+    for s in range(4):
+        assert lib.rettn_status_str(s).decode().startswith("RETTN_")
+
+
+@pytest.mark.parametrize("n", sorted(CONFIGS))
+def test_mask_build_matches_oracle_for_workloads(n):
+    for spec in CONFIGS[n].masks:
+        got = rt.mask_build(spec.kind, spec.nb, spec.w, spec.text_blocks, spec.tshift)
+        ref = om.build_mask(spec.kind, spec.nb, spec.w, spec.text_blocks, spec.tshift)
+        assert np.array_equal(got, ref)
+
+
+def test_mask_build_random_params():
+    rng = np.random.Generator(np.random.PCG64(5))
+    for _ in range(200):
+        kind = int(rng.integers(0, 4))
+        nb = int(rng.integers(1, 60))
+        w = int(rng.integers(1, nb + 1))
+        text = int(rng.integers(0, nb + 1))
+        tshift = int(rng.integers(1, nb + 2))
+        got = rt.mask_build(kind, nb, w, text, tshift)
+        ref = om.build_mask(kind, nb, w, text, tshift)
+        assert np.array_equal(got, ref), (kind, nb, w, text, tshift)
+
+
+@pytest.mark.parametrize("spec", [(7, 4, 1, 0, 0), (b.MASK_BAND, 4, 0, 0, 0), (b.MASK_BAND, 4, 5, 0, 0),
+                                  (b.MASK_COGVIDEO3D, 4, 0, 5, 1), (b.MASK_COGVIDEO3D, 4, 0, 1, 0),
+                                  (b.MASK_DIAG, 0, 0, 0, 0)])
+def test_mask_build_rejects_bad_specs(spec):
+    kind, nb, w, text, tshift = spec
+    out = np.zeros((max(nb, 1), max(nb, 1)), dtype=np.uint8)
+    s = b.MaskSpec(kind, nb, w, text, tshift)
+    assert rt.lib().rettn_mask_build(ctypes.byref(s), out.ctypes.data_as(ctypes.c_void_p)) == EINVAL
+
+
+# ------------------------------------------------------------------ validation (no launch)
+FAKE = 1 << 20   # a 16-byte aligned non-null address; never dereferenced because validation fails first
+
+
+def _good_desc():
+    return b.Desc(2, 3, 200, 64, 64, b.RETTN_BF16, 3 * 200 * 64, 200 * 64, 64)
+
+
+def _idx(nb=4):
+    return b.Index(nb, nb, nb, FAKE, FAKE, FAKE)
+
+
+BAD_DESCS = {
+    "B0": dict(B=0), "L0": dict(L=0), "d0": dict(d=0), "d_big": dict(d=136), "d_not_mult8": dict(d=60),
+    "block48": dict(block=48), "dtype": dict(dtype=7), "stride_l_small": dict(stride_l=32),
+    "stride_misaligned": dict(stride_l=68), "stride_h0": dict(stride_h=0),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BAD_DESCS))
+def test_calibrate_and_sparse_reject_bad_descriptors(name):
+    d = _good_desc()
+    for k, v in BAD_DESCS[name].items():
+        setattr(d, k, v)
+    lib = rt.lib()
+    idx = _idx()
+    assert lib.rettn_calibrate(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(idx), FAKE, FAKE, FAKE, None) == EINVAL
+    assert lib.rettn_sparse(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(idx), FAKE, FAKE, 0.04, 1, FAKE,
+                            None) == EINVAL
+
+
+def test_reject_index_of_wrong_size_and_bad_pointers():
+    lib = rt.lib()
+    d = _good_desc()
+    bad = _idx(3)   # ceil(200 / 64) = 4 blocks
+    assert lib.rettn_calibrate(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(bad), FAKE, FAKE, FAKE, None) == EINVAL
+    idx = _idx()
+    assert lib.rettn_calibrate(ctypes.byref(d), None, FAKE, FAKE, ctypes.byref(idx), FAKE, FAKE, FAKE, None) == EINVAL
+    assert lib.rettn_calibrate(ctypes.byref(d), FAKE + 8, FAKE, FAKE, ctypes.byref(idx), FAKE, FAKE, FAKE,
+                               None) == EINVAL
+    nomask = b.Index(4, 4, 4, FAKE, FAKE, None)
+    assert lib.rettn_calibrate(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(nomask), FAKE, FAKE, FAKE,
+                               None) == EINVAL
+    assert lib.rettn_calibrate(None, FAKE, FAKE, FAKE, ctypes.byref(idx), FAKE, FAKE, FAKE, None) == EINVAL
+
+
+@pytest.mark.parametrize("lam,step", [(-0.1, 1), (float("nan"), 1), (float("inf"), 1), (0.04, -1)])
+def test_sparse_rejects_bad_ramp(lam, step):
+    lib = rt.lib()
+    d = _good_desc()
+    idx = _idx()
+    assert lib.rettn_sparse(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(idx), FAKE, FAKE, lam, step, FAKE,
+                            None) == EINVAL
+
+
+def test_index_build_rejects_bad_arguments():
+    lib = rt.lib()
+    nnz = ctypes.c_int32(-1)
+    assert lib.rettn_index_build(None, 4, 4, FAKE, FAKE, ctypes.byref(nnz), None) == EINVAL
+    assert lib.rettn_index_build(FAKE, 0, 4, FAKE, FAKE, ctypes.byref(nnz), None) == EINVAL
+    assert lib.rettn_index_build(FAKE, 4, 4, FAKE, FAKE, None, None) == EINVAL
+    assert nnz.value == -1

@@ -7,9 +7,9 @@ CPU oracle and the GPU path can take their inputs from it without sharing
 any computation.
 """
 from .configs import CONFIGS, MaskSpec, Config, MASK_DIAG, MASK_BAND, MASK_COGVIDEO3D, MASK_FULL, MASK_CUSTOM
-from .gen import bf16_round, make_qkv, drift, sample_rows
+from .gen import bf16_round, make_qkv, drift, sample_rows, make_cache, random_mask
 
 __all__ = [
     "CONFIGS", "MaskSpec", "Config", "MASK_DIAG", "MASK_BAND", "MASK_COGVIDEO3D", "MASK_FULL", "MASK_CUSTOM",
-    "bf16_round", "make_qkv", "drift", "sample_rows",
+    "bf16_round", "make_qkv", "drift", "sample_rows", "make_cache", "random_mask",
 ]

@@ -10,16 +10,16 @@ import numpy as np
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    nan = np.isnan(x)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
-    out = r.astype(np.uint32).view(np.float32)
-    if nan.any():
-        out = out.copy()
-        out[nan] = np.nan
-    return out
+    """Round finite float32 values to the nearest bfloat16 (ties to even); returns a new float32 array."""
+    x = np.array(x, dtype=np.float32, copy=True, order="C")
+    if not np.isfinite(x).all():
+        raise ValueError("bf16_round expects finite values")
+    u = x.view(np.uint32)
+    lsb = (u >> 16) & np.uint32(1)
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u &= np.uint32(0xFFFF0000)
+    return x
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -60,3 +60,26 @@ def sample_rows(L, block, n, seed):
     fixed.update({last_block_start, max(last_block_start - 1, 0)})
     rest = rng.choice(L, size=min(n, L), replace=False)
     return np.array(sorted(fixed.union(int(x) for x in rest)), dtype=np.int64)
+
+
+def make_cache(B, H, L, d, seed, dtype="bf16"):
+    """A synthetic (rho, R) cache: rho ~ U(0.01, 0.99) float32, R ~ N(0, 0.05^2) in `dtype`.
+
+    Any rho in [0, 1] and any R are valid inputs of a sparse step, so the
+    sparse step can be checked at full size without a full calibration.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed + 5000))
+    rho = rng.uniform(0.01, 0.99, size=(B, H, L)).astype(np.float32)
+    r = _draw(rng, (B, H, L, d), 0.05)
+    if dtype == "bf16":
+        r = bf16_round(r)
+    return rho, r
+
+
+def random_mask(nqb, nkb, density, seed, empty_rows=()):
+    """A seeded random 0/1 block mask (test input), optionally with rows forced empty."""
+    rng = np.random.Generator(np.random.PCG64(seed + 9000))
+    m = (rng.random((nqb, nkb)) < density).astype(np.uint8)
+    for r in empty_rows:
+        m[r, :] = 0
+    return m
