@@ -197,7 +197,7 @@ def main():
     ridge = MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 
     roof_sparse = {"bound": "hbm" if ai_sparse < ridge else "mfma",
-                   "kernel": "attn_bf16_kernel<64,64,sparse>",
+                   "kernel": "sparse64_kernel<64>",
                    "achieved": round(sparse_gbs, 1) if ai_sparse < ridge else round(sparse_tflops, 1),
                    "peak": HBM_PEAK_GBS if ai_sparse < ridge else MFMA_PEAK_TFLOPS,
                    "unit": "GB/s" if ai_sparse < ridge else "TFLOP/s",

@@ -35,6 +35,10 @@ hipError_t launch_sparse_bf16(AttnArgs a, int block, hipStream_t s);
 hipError_t launch_calibrate_f32(AttnArgs a, int block, hipStream_t s);
 hipError_t launch_sparse_f32(AttnArgs a, int block, hipStream_t s);
 
+// One-wave-per-query-block sparse step for 64-token blocks (bfloat16, d <= 64).
+bool sparse64_supported(const AttnArgs& a, int block);
+hipError_t launch_sparse64(AttnArgs a, hipStream_t s);
+
 hipError_t launch_index_build(const uint8_t* mask, int nqb, int nkb, int32_t* row_ptr, int32_t* col_idx,
                               hipStream_t s);
 

@@ -108,10 +108,10 @@ attn_bf16_kernel(const AttnArgs a) {
     if constexpr (CALIB) {
         nit = a.nkb;
     } else {
-        e0 = __builtin_amdgcn_readfirstlane(a.row_ptr[qb]);
-        nit = __builtin_amdgcn_readfirstlane(a.row_ptr[qb + 1]) - e0;
+        e0 = scalar_load(a.row_ptr, qb);
+        nit = scalar_load(a.row_ptr, qb + 1) - e0;
     }
-    const uint8_t* mrow = CALIB ? a.mask + (int64_t)qb * a.nkb : nullptr;
+    const int64_t mrow = (int64_t)qb * a.nkb;   // this wave's mask row (calibration)
 
     f32x16 acc[C::NDT];
     f32x16 acc2[CALIB ? C::NDT : 1];   // calibration: masked-key accumulator
@@ -154,7 +154,7 @@ attn_bf16_kernel(const AttnArgs a) {
     };
     auto kb_of = [&](int it) -> int {
         if constexpr (CALIB) return it;
-        else return __builtin_amdgcn_readfirstlane(a.col_idx[e0 + it]);
+        else return scalar_load(a.col_idx, e0 + it);
     };
 
     // Lane-constant parts of the LDS fragment addresses.
@@ -226,7 +226,7 @@ attn_bf16_kernel(const AttnArgs a) {
         dsum2 *= alpha;
 
         bool in_window = true;
-        if constexpr (CALIB) in_window = mrow[kb] != 0;
+        if constexpr (CALIB) in_window = scalar_load(a.mask, mrow + kb) != 0;
         if (in_window) dsum += psum;
         else dsum2 += psum;
 
@@ -337,6 +337,9 @@ static hipError_t dispatch(AttnArgs a, int block, hipStream_t s) {
 }
 
 hipError_t launch_calibrate_bf16(AttnArgs a, int block, hipStream_t s) { return dispatch<true>(a, block, s); }
-hipError_t launch_sparse_bf16(AttnArgs a, int block, hipStream_t s) { return dispatch<false>(a, block, s); }
+hipError_t launch_sparse_bf16(AttnArgs a, int block, hipStream_t s) {
+    if (sparse64_supported(a, block)) return launch_sparse64(a, s);
+    return dispatch<false>(a, block, s);
+}
 
 }  // namespace rettn

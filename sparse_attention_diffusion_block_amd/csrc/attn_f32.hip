@@ -85,10 +85,10 @@ attn_f32_kernel(const AttnArgs a) {
     if constexpr (CALIB) {
         nit = a.nkb;
     } else {
-        e0 = __builtin_amdgcn_readfirstlane(a.row_ptr[qb]);
-        nit = __builtin_amdgcn_readfirstlane(a.row_ptr[qb + 1]) - e0;
+        e0 = scalar_load(a.row_ptr, qb);
+        nit = scalar_load(a.row_ptr, qb + 1) - e0;
     }
-    const uint8_t* mrow = CALIB ? a.mask + (int64_t)qb * a.nkb : nullptr;
+    const int64_t mrow = (int64_t)qb * a.nkb;   // this wave's mask row (calibration)
 
     f32x16 acc[C::NDT];
     f32x16 acc2[CALIB ? C::NDT : 1];
@@ -134,7 +134,7 @@ attn_f32_kernel(const AttnArgs a) {
     };
     auto kb_of = [&](int it) -> int {
         if constexpr (CALIB) return it;
-        else return __builtin_amdgcn_readfirstlane(a.col_idx[e0 + it]);
+        else return scalar_load(a.col_idx, e0 + it);
     };
 
     if (nit > 0) {
@@ -193,7 +193,7 @@ attn_f32_kernel(const AttnArgs a) {
         dsum *= alpha;
         dsum2 *= alpha;
         bool in_window = true;
-        if constexpr (CALIB) in_window = mrow[kb] != 0;
+        if constexpr (CALIB) in_window = scalar_load(a.mask, mrow + kb) != 0;
         if (in_window) dsum += psum;
         else dsum2 += psum;
 

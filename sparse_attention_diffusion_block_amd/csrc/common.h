@@ -38,7 +38,7 @@ __device__ __forceinline__ int xcd_remap(int wg, int total) {
 //     ds_read_b64_tr_b16 of a V operand fragment (16 lanes, 4 keys x 32 bytes)
 //     is conflict-free.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int swz(int key) { return ((key & 3) << 1) | ((key >> 2) & 1); }
+__host__ __device__ __forceinline__ int swz(int key) { return ((key & 3) << 1) | ((key >> 2) & 1); }
 
 __device__ __forceinline__ float xhalf_max(float x) {
     // lanes l and l^32 hold the two halves of one query row's keys
@@ -52,6 +52,15 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Wave-uniform reads of read-only tables (CSR row pointers and column ids,
+// mask bytes) through the constant address space: they become scalar loads,
+// which are counted by lgkmcnt, so waiting for them never drains the vector
+// loads (K/V prefetches) that are in flight.
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+typedef const __attribute__((address_space(4))) uint8_t* const_u8_ptr;
+__device__ __forceinline__ int32_t scalar_load(const int32_t* p, int64_t i) { return ((const_i32_ptr)p)[i]; }
+__device__ __forceinline__ uint8_t scalar_load(const uint8_t* p, int64_t i) { return ((const_u8_ptr)p)[i]; }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -1,0 +1,312 @@
+// Sparse step of Re-ttention for bfloat16 with 64-token blocks, one wave per
+// query block.
+//
+// The step (Re-ttention summary page, "Approach"; review thread, replies to
+// W1 of the first and third reviews; ramp-up: answer to W1 of the fourth
+// review) attends each 64-row query block only to its kept key blocks (the
+// CSR row), then applies the statistical reshape and the residual:
+//     O' = min(1, rho * (1 + lambda step)) * softmax_W(s) V_W + R.
+//
+// Design for gfx950 (HBM- and latency-bound at 96.9% sparsity):
+//   * one wave owns all 64 rows of a query block, so the K and V of a key
+//     block are fetched once per query block and no barrier is ever needed;
+//   * K arrives by 16-byte buffer loads straight into the A fragments of
+//     S^T = K Q^T (d is contiguous, which is the layout the fragment needs);
+//     padding and keys past L read as zero through the buffer bounds;
+//   * V streams straight into LDS (buffer_load ... lds, double buffered, one
+//     key block ahead) and comes back through the transposing LDS read as
+//     the V^T fragments of O^T += V^T P^T;
+//   * P*V runs in float16 (P rounds 8x finer than in bfloat16); V is
+//     re-encoded exactly as its fragments are read;
+//   * the softmax keeps a running reference per row instead of a per-block
+//     max: a block's probabilities are computed against the current
+//     reference, and only if a row's packed float16 sum is non-finite or
+//     above 2^14 is the block redone against its true max (rescaling the
+//     accumulators).  Any reference gives the same mathematics; the bound
+//     keeps every float16 probability finite.
+#include "attn.h"
+#include "common.h"
+
+namespace rettn {
+
+namespace {
+
+constexpr uint32_t kOOB = 0x80000000u;   // a buffer offset past every record: reads as zero
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t f16x2_from_bf16x2(uint32_t w) { return pack_f16(bf16_lo(w), bf16_hi(w)); }
+
+__device__ __forceinline__ float dot2_f16(uint32_t a, float acc) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, a), one, acc, false);
+}
+
+}  // namespace
+
+template <int DP>
+struct S64Cfg {
+    static constexpr int NS = DP / 16;             // k-steps of S^T over d
+    static constexpr int NDT = DP / 32;            // 32-row d tiles of O^T
+    static constexpr int RS = 64;                  // LDS row stride (elements): one 128-byte row
+    static constexpr int SLOT = 64 * RS;           // elements per 64-row LDS slot (8 KiB)
+    static constexpr int NL = 8;                   // 1 KiB transfers per 64-row tile
+};
+
+// All global traffic moves as 64-row tiles of 128-byte rows, 1 KiB per
+// instruction: lane l carries 16 bytes of row 8 i + l / 8, so each group of
+// 8 lanes covers one contiguous row.  In LDS, logical 16-byte chunk c of row
+// r sits at physical chunk c ^ swz(r) (see common.h).  A tile transfer of a
+// padded chunk or of a row at or past L uses an offset past the buffer
+// records: loads read zeros, stores are dropped.
+template <int DP>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) sparse64_kernel(const AttnArgs a) {
+    using C = S64Cfg<DP>;
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * C::SLOT];
+    uint16_t* const kslot = lds;              // K tiles (and Q at the start)
+    uint16_t* const vslot = lds + C::SLOT;    // V tiles (and R, then O, at the end)
+
+    const int lane = threadIdx.x;
+    const int h = lane >> 5, n = lane & 31;
+    const int work = xcd_remap(blockIdx.x, a.G);
+    const int bh = work / a.nqb;
+    const int qb = work - bh * a.nqb;
+    const int bi = bh / a.H, hi = bh - bi * a.H;
+    const int64_t base = (int64_t)bi * a.sb + (int64_t)hi * a.sh;
+    const int q0 = qb * 64;
+    const uint32_t row_bytes = (uint32_t)a.sl * 2u;
+    // one (batch, head) slice: rows [0, L) of d elements
+    const uint32_t nrec = (uint32_t)(a.L - 1) * row_bytes + (uint32_t)a.d * 2u;
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)a.Q + base), 0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)a.K + base), 0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)a.V + base), 0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)a.R_in + base), 0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc((void*)((uint16_t*)a.O + base), 0, nrec, 0x00020000);
+
+    // lane -> (row within an 8-row group, physical chunk) of a tile transfer
+    const int trow = lane >> 3, tpc = lane & 7;
+#define RETTN_TILE_OFF(ROW0, I)                                                                \
+    ((tpc ^ swz(8 * (I) + trow)) * 8 < a.d                                                       \
+         ? (uint32_t)((ROW0) + 8 * (I) + trow) * row_bytes + 16u * (uint32_t)(tpc ^ swz(8 * (I) + trow)) \
+         : kOOB)
+    // (plain expressions only inside these loaders: a lambda called from another
+    // lambda here, a buffer-resource lambda parameter or a generic pointer cast to
+    // the LDS address space keeps the host compiler from emitting the launch stub)
+#define RETTN_TILE_LOADER(NAME, RSRC)                                                                             \
+    auto NAME = [&](int row0, int slot) {                                                                        \
+        _Pragma("unroll") for (int i = 0; i < C::NL; ++i)                                                         \
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                             \
+                RSRC, (__attribute__((address_space(3))) void*)(lds + slot * C::SLOT + i * 512), 16, RETTN_TILE_OFF(row0, i), \
+                0, 0, 0);                                                                                         \
+    };
+    RETTN_TILE_LOADER(load_q, rq)
+    RETTN_TILE_LOADER(load_k, rk)
+    RETTN_TILE_LOADER(load_v, rv)
+    RETTN_TILE_LOADER(load_r, rr)
+#undef RETTN_TILE_LOADER
+    // fragment of row r, logical chunk c (16 bytes)
+    auto frag = [&](const uint16_t* slot, int r, int c) -> u32x4 {
+        return *(const u32x4*)(slot + r * C::RS + ((c ^ swz(r)) << 3));
+    };
+
+    const int e0 = scalar_load(a.row_ptr, qb);
+    const int nit = scalar_load(a.row_ptr, qb + 1) - e0;
+
+    // Q tile -> registers: B operand of S^T = K Q^T, Q[q0 + 32 rt + n][16 s + 8 h .. +7]
+    load_q(q0, 0);
+    wait_vmcnt<0>();
+    u32x4 qf[2][C::NS];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int s = 0; s < C::NS; ++s) qf[rt][s] = frag(kslot, 32 * rt + n, 2 * s + h);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+
+    f32x16 acc[C::NDT][2];
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) acc[dt][0] = acc[dt][1] = f32x16{};
+    float mref[2] = {-INFINITY, -INFINITY};   // running reference, log2 units
+    float dsum[2] = {0.f, 0.f};
+
+    int kbn = 0;
+    if (nit > 0) {
+        kbn = scalar_load(a.col_idx, e0);
+        load_k(kbn * 64, 0);
+        load_v(kbn * 64, 1);
+    }
+
+    // lane-constant parts of the transposing V reads
+    const int s16 = lane & 15, g = lane >> 4;
+    const int fv = ((s16 >> 2) << 1) | h;
+    const int vrow = (4 * h + (s16 >> 2)) * C::RS;
+
+    // In flight at the top of iteration it: K(it), then V(it).
+    for (int it = 0; it < nit; ++it) {
+        const int kb = kbn;
+        const bool more = it + 1 < nit;
+        kbn = more ? scalar_load(a.col_idx, e0 + it + 1) : 0;
+
+        wait_vmcnt<C::NL>();                      // K(it) has landed (V(it) may still be in flight)
+        u32x4 kf[2][C::NS];                       // A operand: K[64 kb + 32 kt + n][16 s + 8 h .. +7]
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int s = 0; s < C::NS; ++s) kf[kt][s] = frag(kslot, 32 * kt + n, 2 * s + h);
+
+        u32x4 pf[2][4];
+        const bool tail = __builtin_expect((kb + 1) * 64 > a.L, 0);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            f32x16 sacc[2];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                sacc[kt] = f32x16{};
+#pragma unroll
+                for (int s = 0; s < C::NS; ++s)
+                    sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, kf[kt][s]), __builtin_bit_cast(bf16x8, qf[rt][s]), sacc[kt], 0, 0, 0);
+            }
+            if (rt == 1 && more) {
+                // the K fragments are in registers: refill the K slot with the next key block
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                load_k(kbn * 64, 0);
+            }
+            if (tail) {
+                int lim = a.L - kb * 64 - 4 * h;   // keys at local index >= lim do not exist
+                asm volatile("" : "+v"(lim));      // keeps the compares inside this rarely taken branch
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        if (kt * 32 + 8 * (j >> 2) + (j & 3) >= lim) sacc[kt][j] = -INFINITY;
+            }
+            float bsum;
+            auto make_p = [&]() {
+                float sum = 0.f;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const f32x16& sp = sacc[t >> 1];
+                    const int o8 = 8 * (t & 1);
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const float p0 = fast_exp2(fmaf(sp[o8 + 2 * w], a.c, -mref[rt]));
+                        const float p1 = fast_exp2(fmaf(sp[o8 + 2 * w + 1], a.c, -mref[rt]));
+                        pf[rt][t][w] = pack_f16(p0, p1);
+                        sum = dot2_f16(pf[rt][t][w], sum);
+                    }
+                }
+                bsum = sum;
+            };
+            make_p();
+            if (__builtin_amdgcn_ballot_w64(!(bsum <= 16384.f)) != 0) {
+                // re-anchor the reference at the true running max and redo this tile
+                float bm = -INFINITY;
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) bm = fmaxf(bm, sacc[kt][j]);
+                bm = xhalf_max(bm) * a.c;
+                const float mnew = fmaxf(mref[rt], bm);
+                const float alpha = fast_exp2(mref[rt] - mnew);
+                mref[rt] = mnew;
+                dsum[rt] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < C::NDT; ++dt) acc[dt][rt] *= alpha;
+                make_p();
+            }
+            dsum[rt] += bsum;
+        }
+
+        // V(it) has landed once at most the K(it+1) refill is still in flight
+        if (more) wait_vmcnt<C::NL>();
+        else wait_vmcnt<0>();
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt) {
+                const int c = 4 * dt + 2 * (g & 1) + ((s16 & 3) >> 1);
+                const uint16_t* p = vslot + vrow + 16 * t * C::RS + ((c ^ fv) << 3) + ((s16 & 1) << 2);
+                const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)p);
+                const i16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(p + 8 * C::RS));
+                const u32x2 w1 = __builtin_bit_cast(u32x2, r1), w2 = __builtin_bit_cast(u32x2, r2);
+                u32x4 vw;
+                vw[0] = f16x2_from_bf16x2(w1[0]);
+                vw[1] = f16x2_from_bf16x2(w1[1]);
+                vw[2] = f16x2_from_bf16x2(w2[0]);
+                vw[3] = f16x2_from_bf16x2(w2[1]);
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+                    acc[dt][rt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        __builtin_bit_cast(f16x8, vw), __builtin_bit_cast(f16x8, pf[rt][t]), acc[dt][rt], 0, 0, 0);
+            }
+        }
+        // the V fragments are read: refill the V slot with the next key block
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (more) load_v(kbn * 64, 1);
+    }
+
+    // Epilogue: O' = min(1, rho * ramp) * acc / D' + R, transposed through LDS so
+    // that R is read and O written as whole 128-byte rows.
+    wait_vmcnt<0>();
+    load_r(q0, 1);
+    float scale[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        const int row = q0 + 32 * rt + n;
+        const float rho = row < a.L ? a.rho_in[(int64_t)bh * a.L + row] : 0.f;
+        const float dtot = xhalf_sum(dsum[rt]);
+        scale[rt] = nit > 0 ? fminf(1.f, rho * a.ramp) / dtot : 0.f;
+    }
+    wait_vmcnt<0>();
+    // lane (n, h) owns d = 32 dt + 8 bb + 4 h + r of rows 32 rt + n: read R there, write O there
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                const int r = 32 * rt + n;
+                uint16_t* p = vslot + r * C::RS + (((4 * dt + bb) ^ swz(r)) << 3) + 4 * h;
+                const u32x2 rw = *(const u32x2*)p;
+                const int j = 4 * bb;
+                u32x2 ow;
+                ow[0] = pack_bf16(fmaf(scale[rt], acc[dt][rt][j], bf16_lo(rw[0])),
+                                  fmaf(scale[rt], acc[dt][rt][j + 1], bf16_hi(rw[0])));
+                ow[1] = pack_bf16(fmaf(scale[rt], acc[dt][rt][j + 2], bf16_lo(rw[1])),
+                                  fmaf(scale[rt], acc[dt][rt][j + 3], bf16_hi(rw[1])));
+                *(u32x2*)p = ow;
+            }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < C::NL; ++i) {
+        const u32x4 w = *(const u32x4*)(vslot + (8 * i + trow) * C::RS + tpc * 8);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), ro, RETTN_TILE_OFF(q0, i), 0, 0);
+    }
+#undef RETTN_TILE_OFF
+}
+
+template <int DP>
+static hipError_t launch(AttnArgs a, hipStream_t s) {
+    const int64_t G = (int64_t)a.B * a.H * a.nqb;
+    if (G <= 0 || G > 0x7fffffff) return hipErrorInvalidValue;
+    a.G = (int32_t)G;
+    hipLaunchKernelGGL((sparse64_kernel<DP>), dim3((unsigned)G), dim3(64), 0, s, a);
+    return hipGetLastError();
+}
+
+bool sparse64_supported(const AttnArgs& a, int block) {
+    // buffer offsets are 32-bit: one (batch, head) slice must stay below 2 GiB
+    const int64_t slice = ((int64_t)a.L - 1) * a.sl * 2 + (int64_t)a.d * 2;
+    return block == 64 && a.d <= 64 && slice < ((int64_t)1 << 31);
+}
+
+hipError_t launch_sparse64(AttnArgs a, hipStream_t s) {
+    return pad_d(a.d) <= 32 ? launch<32>(a, s) : launch<64>(a, s);
+}
+
+}  // namespace rettn

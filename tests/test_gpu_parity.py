@@ -69,6 +69,10 @@ SMALL = [
     ("bf16-cog-d16", "bf16", 1, 1, 500, 16, 32, lambda nb: om.cogvideo3d_mask(nb, 2, 5)),
     ("bf16-full-L1", "bf16", 1, 1, 1, 64, 32, lambda nb: om.full_mask(nb)),
     ("bf16-full-d128", "bf16", 1, 2, 200, 128, 64, lambda nb: om.full_mask(nb)),
+    ("bf16-b64-d48-emptyrow", "bf16", 2, 2, 450, 48, 64, lambda nb: random_mask(nb, nb, 0.4, 14, empty_rows=(3,))),
+    ("bf16-b64-d32-full", "bf16", 1, 2, 200, 32, 64, lambda nb: om.full_mask(nb)),
+    ("bf16-b64-d64-full", "bf16", 1, 1, 256, 64, 64, lambda nb: om.full_mask(nb)),
+    ("bf16-b64-d64-cog-tail", "bf16", 2, 2, 1000, 64, 64, lambda nb: om.cogvideo3d_mask(nb, 2, 4)),
     ("f32-rand-L257", "f32", 1, 2, 257, 64, 64, lambda nb: random_mask(nb, nb, 0.4, 13, empty_rows=(2,))),
     ("f32-band-d96-block128", "f32", 2, 1, 190, 96, 128, lambda nb: om.band_mask(nb, 1)),
     ("f32-full-d8", "f32", 1, 1, 100, 8, 32, lambda nb: om.full_mask(nb)),
@@ -76,10 +80,12 @@ SMALL = [
 ]
 
 
-def _run_small(rt, dtype, B, H, L, d, block, make_mask, seed):
+def _run_small(rt, dtype, B, H, L, d, block, make_mask, seed, qk_scale=1.0):
     import torch
     scale = 1.0 / math.sqrt(d) if dtype == "f32" else 1.0
     q, k, v = make_qkv(B, H, L, d, seed, scale=scale, dtype=dtype)
+    if qk_scale != 1.0:
+        q, k = (bf16_round(x * np.float32(qk_scale)) if dtype == "bf16" else x * np.float32(qk_scale) for x in (q, k))
     nb = -(-L // block)
     mask = make_mask(nb)
     idx = rt.index_build(mask, block)
@@ -106,6 +112,14 @@ def test_small_case_all_rows(rt, case):
     name, dtype, B, H, L, d, block, make_mask = case
     log(f"case {name}: dtype={dtype} B={B} H={H} L={L} d={d} block={block}")
     _run_small(rt, dtype, B, H, L, d, block, make_mask, seed=hash(name) % 1000)
+
+
+@pytest.mark.parametrize("d,block", [(64, 64), (72, 64), (128, 128)])
+def test_large_scores_rescale_path(rt, d, block):
+    """Q and K scaled by 3 give scores of standard deviation ~9: later key blocks exceed the
+    running reference by far, which forces the softmax to re-anchor and rescale."""
+    log(f"case large-scores d={d} block={block}")
+    _run_small(rt, "bf16", 1, 2, 640, d, block, lambda nb: om.band_mask(nb, 5), seed=77, qk_scale=3.0)
 
 
 # ------------------------------------------------------------------ worked example, block-lifted
@@ -152,11 +166,10 @@ def test_worked_example_lifted(rt, dtype, golden):
 
 
 # ------------------------------------------------------------------ determinism
-def test_bitwise_deterministic(rt):
+@pytest.mark.parametrize("d", [64, 72])
+def test_bitwise_deterministic(rt, d):
     import torch
-    cfg = CONFIGS[2]
-    q, k, v = make_qkv(1, 4, 1000, 72, 3)
-    spec = cfg.masks[0]
+    q, k, v = make_qkv(1, 4, 1000, d, 3)
     nb = -(-1000 // 64)
     mask = om.band_mask(nb, 2)
     idx = rt.index_build(mask, 64)
