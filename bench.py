@@ -205,7 +205,7 @@ def main():
                    "mfma_frac": round(sparse_tflops / MFMA_PEAK_TFLOPS, 4),
                    "ms": round(t_sp * 1e3, 4)}
     roof_sparse["frac"] = round(roof_sparse["achieved"] / roof_sparse["peak"], 4)
-    roof_cal = {"bound": "mfma", "kernel": "attn_bf16_kernel<64,64,calibrate>",
+    roof_cal = {"bound": "mfma", "kernel": "calib_kernel<64,64>",
                 "achieved": round(calib_tflops, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(calib_tflops / MFMA_PEAK_TFLOPS, 4), "traffic": None,
                 "ms": round(t_cal * 1e3, 4)}

@@ -39,6 +39,10 @@ hipError_t launch_sparse_f32(AttnArgs a, int block, hipStream_t s);
 bool sparse64_supported(const AttnArgs& a, int block);
 hipError_t launch_sparse64(AttnArgs a, hipStream_t s);
 
+// Calibration for 64- and 128-token blocks (bfloat16): 256 query rows per work-group.
+bool calib_supported(const AttnArgs& a, int block);
+hipError_t launch_calib(AttnArgs a, int block, hipStream_t s);
+
 hipError_t launch_index_build(const uint8_t* mask, int nqb, int nkb, int32_t* row_ptr, int32_t* col_idx,
                               hipStream_t s);
 

@@ -336,7 +336,10 @@ static hipError_t dispatch(AttnArgs a, int block, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_calibrate_bf16(AttnArgs a, int block, hipStream_t s) { return dispatch<true>(a, block, s); }
+hipError_t launch_calibrate_bf16(AttnArgs a, int block, hipStream_t s) {
+    if (calib_supported(a, block)) return launch_calib(a, block, s);
+    return dispatch<true>(a, block, s);
+}
 hipError_t launch_sparse_bf16(AttnArgs a, int block, hipStream_t s) {
     if (sparse64_supported(a, block)) return launch_sparse64(a, s);
     return dispatch<false>(a, block, s);
