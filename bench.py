@@ -196,18 +196,27 @@ def main():
     ai_sparse = f_sparse / bytes_alg
     ridge = MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 
+    from sparse_attention_diffusion_block_amd.profiling import kernel_source_hash, read_traffic
+    traffic = read_traffic(os.path.join(ROOT, "profiles", f"hbm_traffic_{cfg.name}.txt"))
+
+    def traffic_of(kernel):
+        """Counter-measured HBM bytes per launch, if taken on the current source of the kernel."""
+        sha, nbytes = traffic.get(kernel, (None, None))
+        return nbytes if sha is not None and sha == kernel_source_hash(kernel) else None
+
+    k_sparse, k_cal = "sparse64_kernel<64>", "calib_kernel<64, 64>"
     roof_sparse = {"bound": "hbm" if ai_sparse < ridge else "mfma",
-                   "kernel": "sparse64_kernel<64>",
+                   "kernel": k_sparse,
                    "achieved": round(sparse_gbs, 1) if ai_sparse < ridge else round(sparse_tflops, 1),
                    "peak": HBM_PEAK_GBS if ai_sparse < ridge else MFMA_PEAK_TFLOPS,
                    "unit": "GB/s" if ai_sparse < ridge else "TFLOP/s",
-                   "traffic": None,
+                   "traffic": traffic_of(k_sparse),
                    "mfma_frac": round(sparse_tflops / MFMA_PEAK_TFLOPS, 4),
                    "ms": round(t_sp * 1e3, 4)}
     roof_sparse["frac"] = round(roof_sparse["achieved"] / roof_sparse["peak"], 4)
-    roof_cal = {"bound": "mfma", "kernel": "calib_kernel<64,64>",
+    roof_cal = {"bound": "mfma", "kernel": k_cal,
                 "achieved": round(calib_tflops, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(calib_tflops / MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                "frac": round(calib_tflops / MFMA_PEAK_TFLOPS, 4), "traffic": traffic_of(k_cal),
                 "ms": round(t_cal * 1e3, 4)}
     # the dominant kernel of a step is the one with the larger share of its time
     dominant_is_cal = t_cal > T * t_sp
