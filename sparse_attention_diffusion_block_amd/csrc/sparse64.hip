@@ -7,15 +7,19 @@
 // CSR row), then applies the statistical reshape and the residual:
 //     O' = min(1, rho * (1 + lambda step)) * softmax_W(s) V_W + R.
 //
-// Design for gfx950 (HBM- and latency-bound at 96.9% sparsity):
+// Design for gfx950 (at 96.9% sparsity the step is bound by memory latency
+// and by the vector work of the softmax, not by the matrix cores):
 //   * one wave owns all 64 rows of a query block, so the K and V of a key
 //     block are fetched once per query block and no barrier is ever needed;
-//   * K arrives by 16-byte buffer loads straight into the A fragments of
-//     S^T = K Q^T (d is contiguous, which is the layout the fragment needs);
-//     padding and keys past L read as zero through the buffer bounds;
-//   * V streams straight into LDS (buffer_load ... lds, double buffered, one
-//     key block ahead) and comes back through the transposing LDS read as
-//     the V^T fragments of O^T += V^T P^T;
+//   * every tile (Q, K, V, R) streams straight into LDS (buffer_load ... lds,
+//     1 KiB per instruction); padding and keys past L read as zero through
+//     the buffer bounds.  K comes back as the A fragments of S^T = K Q^T, V
+//     through the transposing LDS read as the V^T fragments of
+//     O^T += V^T P^T.  Each slot is refilled with the next key block as soon
+//     as its fragments are in registers;
+//   * the MFMAs of one row tile are interleaved with independent vector work
+//     (the float16 re-encoding of V, the probabilities of the other row
+//     tile), which a wave issues while its MFMAs execute;
 //   * P*V runs in float16 (P rounds 8x finer than in bfloat16); V is
 //     re-encoded exactly as its fragments are read;
 //   * the softmax keeps a running reference per row instead of a per-block
@@ -67,9 +71,10 @@ struct S64Cfg {
 template <int DP>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) sparse64_kernel(const AttnArgs a) {
     using C = S64Cfg<DP>;
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * C::SLOT];
-    uint16_t* const kslot = lds;              // K tiles (and Q at the start)
-    uint16_t* const vslot = lds + C::SLOT;    // V tiles (and R, then O, at the end)
+    // Two separate LDS objects: the compiler can then tell that a transfer into one
+    // slot never overlaps reads of the other, and does not wait for it.
+    __shared__ __attribute__((aligned(1024))) uint16_t kslot[C::SLOT];   // K tiles
+    __shared__ __attribute__((aligned(1024))) uint16_t vslot[C::SLOT];   // V tiles; Q at the start, R / O at the end
 
     const int lane = threadIdx.x;
     const int h = lane >> 5, n = lane & 31;
@@ -90,24 +95,25 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
     // lane -> (row within an 8-row group, physical chunk) of a tile transfer
     const int trow = lane >> 3, tpc = lane & 7;
-#define RETTN_TILE_OFF(ROW0, I)                                                                \
-    ((tpc ^ swz(8 * (I) + trow)) * 8 < a.d                                                       \
-         ? (uint32_t)((ROW0) + 8 * (I) + trow) * row_bytes + 16u * (uint32_t)(tpc ^ swz(8 * (I) + trow)) \
-         : kOOB)
+    // (select by arithmetic, not by a conditional: a conditional offset here is turned
+    // into exec-masked branches around the transfer)
+#define RETTN_TILE_OFF(ROW0, I)                                                                        \
+    ((((uint32_t)((ROW0) + 8 * (I) + trow) * row_bytes + 16u * (uint32_t)(tpc ^ swz(8 * (I) + trow))) & \
+      (0u - (uint32_t)((tpc ^ swz(8 * (I) + trow)) * 8 < a.d))) |                                          \
+     (kOOB & ((uint32_t)((tpc ^ swz(8 * (I) + trow)) * 8 < a.d) - 1u)))
     // (plain expressions only inside these loaders: a lambda called from another
     // lambda here, a buffer-resource lambda parameter or a generic pointer cast to
     // the LDS address space keeps the host compiler from emitting the launch stub)
-#define RETTN_TILE_LOADER(NAME, RSRC)                                                                             \
-    auto NAME = [&](int row0, int slot) {                                                                        \
+#define RETTN_TILE_LOADER(NAME, RSRC, SLOT)                                                                   \
+    auto NAME = [&](int row0) {                                                                                  \
         _Pragma("unroll") for (int i = 0; i < C::NL; ++i)                                                         \
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                             \
-                RSRC, (__attribute__((address_space(3))) void*)(lds + slot * C::SLOT + i * 512), 16, RETTN_TILE_OFF(row0, i), \
-                0, 0, 0);                                                                                         \
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(RSRC, (__attribute__((address_space(3))) void*)(SLOT + i * 512), \
+                                                     16, RETTN_TILE_OFF(row0, i), 0, 0, 0);                      \
     };
-    RETTN_TILE_LOADER(load_q, rq)
-    RETTN_TILE_LOADER(load_k, rk)
-    RETTN_TILE_LOADER(load_v, rv)
-    RETTN_TILE_LOADER(load_r, rr)
+    RETTN_TILE_LOADER(load_q, rq, vslot)
+    RETTN_TILE_LOADER(load_k, rk, kslot)
+    RETTN_TILE_LOADER(load_v, rv, vslot)
+    RETTN_TILE_LOADER(load_r, rr, vslot)
 #undef RETTN_TILE_LOADER
     // fragment of row r, logical chunk c (16 bytes)
     auto frag = [&](const uint16_t* slot, int r, int c) -> u32x4 {
@@ -118,151 +124,204 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int nit = scalar_load(a.row_ptr, qb + 1) - e0;
 
     // Q tile -> registers: B operand of S^T = K Q^T, Q[q0 + 32 rt + n][16 s + 8 h .. +7]
-    load_q(q0, 0);
-    wait_vmcnt<0>();
+    // rho of this wave's rows (used in the epilogue; issued first so it is long done by then)
+    float rho_r[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        const int row = q0 + 32 * rt + n;
+        rho_r[rt] = row < a.L ? a.rho_in[(int64_t)bh * a.L + row] : 0.f;
+    }
+    // Q tile into the V slot and the first K tile into the K slot, together
+    int kbn = nit > 0 ? scalar_load(a.col_idx, e0) : 0;
+    load_q(q0);
+    if (nit > 0) {
+        load_k(kbn * 64);
+        wait_vmcnt<C::NL>();                  // Q has landed (K may still be in flight)
+    } else {
+        wait_vmcnt<0>();
+    }
     u32x4 qf[2][C::NS];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int s = 0; s < C::NS; ++s) qf[rt][s] = frag(kslot, 32 * rt + n, 2 * s + h);
+        for (int s = 0; s < C::NS; ++s) qf[rt][s] = frag(vslot, 32 * rt + n, 2 * s + h);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (nit > 0) load_v(kbn * 64);         // in flight now: K(0), then V(0)
+    else load_r(q0);
 
     f32x16 acc[C::NDT][2];
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt) acc[dt][0] = acc[dt][1] = f32x16{};
-    float mref[2] = {-INFINITY, -INFINITY};   // running reference, log2 units
+    // Running reference per row, log2 units.  It starts at -inf, so the first kept
+    // block always takes the re-anchoring path below and anchors at its own max.
+    float mref[2] = {-INFINITY, -INFINITY};
     float dsum[2] = {0.f, 0.f};
-
-    int kbn = 0;
-    if (nit > 0) {
-        kbn = scalar_load(a.col_idx, e0);
-        load_k(kbn * 64, 0);
-        load_v(kbn * 64, 1);
-    }
 
     // lane-constant parts of the transposing V reads
     const int s16 = lane & 15, g = lane >> 4;
     const int fv = ((s16 >> 2) << 1) | h;
     const int vrow = (4 * h + (s16 >> 2)) * C::RS;
 
-    // In flight at the top of iteration it: K(it), then V(it).
-    for (int it = 0; it < nit; ++it) {
-        const int kb = kbn;
-        const bool more = it + 1 < nit;
-        kbn = more ? scalar_load(a.col_idx, e0 + it + 1) : 0;
-
-        wait_vmcnt<C::NL>();                      // K(it) has landed (V(it) may still be in flight)
-        u32x4 kf[2][C::NS];                       // A operand: K[64 kb + 32 kt + n][16 s + 8 h .. +7]
+    f32x16 sacc[2][2];                            // [row tile][key tile]
+    u32x4 pf[2][4];                               // P^T fragments (float16) of both row tiles
+    float bsum[2];
+    // probabilities of pairs [p0, p1) of row tile rt (pair 4 t + w covers the two
+    // scores that pack into pf[rt][t][w]) against the running reference, in float16;
+    // their float16 sum accumulates into bsum[rt]
+    auto make_p = [&](int rt, int p0, int p1) {
+#pragma unroll
+        for (int pi = p0; pi < p1; ++pi) {
+            const int t = pi >> 2, w = pi & 3;
+            const f32x16& sp = sacc[rt][t >> 1];
+            const int o = 8 * (t & 1) + 2 * w;
+            const float e0 = fast_exp2(fmaf(sp[o], a.c, -mref[rt]));
+            const float e1 = fast_exp2(fmaf(sp[o + 1], a.c, -mref[rt]));
+            pf[rt][t][w] = pack_f16(e0, e1);
+            bsum[rt] = dot2_f16(pf[rt][t][w], bsum[rt]);
+        }
+    };
+    // re-anchor the reference of row tile rt at the true running max (rescaling what is
+    // accumulated), then redo its probabilities
+    auto reanchor = [&](int rt) {
+        float bm = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int s = 0; s < C::NS; ++s) kf[kt][s] = frag(kslot, 32 * kt + n, 2 * s + h);
+            for (int j = 0; j < 16; ++j) bm = fmaxf(bm, sacc[rt][kt][j]);
+        bm = xhalf_max(bm) * a.c;
+        const float mnew = fmaxf(mref[rt], bm);
+        const float alpha = fast_exp2(mref[rt] - mnew);
+        mref[rt] = mnew;
+        dsum[rt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt) acc[dt][rt] *= alpha;
+        bsum[rt] = 0.f;
+        make_p(rt, 0, 16);
+    };
+    // keys at or past L in the last key block take -inf scores
+    auto mask_tail = [&](int rt, int kb) {
+        int lim = a.L - kb * 64 - 4 * h;   // keys at local index >= lim do not exist
+        asm volatile("" : "+v"(lim));      // keeps the compares inside the rarely taken branch
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                if (kt * 32 + 8 * (j >> 2) + (j & 3) >= lim) sacc[rt][kt][j] = -INFINITY;
+    };
 
-        u32x4 pf[2][4];
-        const bool tail = __builtin_expect((kb + 1) * 64 > a.L, 0);
+    // MFMAs per phase and the share of vector work issued behind each of them
+    constexpr int NA = 2 * C::NS;                 // S^T MFMAs of one row tile
+    constexpr int NC = 4 * C::NDT;                // P*V MFMAs of one row tile
+    constexpr int VA = 16 * C::NDT / NA;          // V registers re-encoded per MFMA of phase A
+    constexpr int PB = 16 / NA, PC = 16 / NC;     // probability pairs per MFMA of phases B and C
+    static_assert(VA * NA == 16 * C::NDT && PB * NA == 16 && PC * NC == 16, "phase split");
+
+    // In flight at the top of iteration it: K(it), then V(it).  Each iteration runs in
+    // four phases; in each, every MFMA is followed by a fixed share of independent
+    // vector work of the same wave, which issues while the MFMA executes:
+    //   A  S^T of row tile 0            | V(it) fragments re-encoded to float16
+    //      (then the K and V slots are refilled with the next key block, or the V slot
+    //       with this query block's residual R after the last one)
+    //   B  S^T of row tile 1            | probabilities of row tile 0
+    //   C  O^T += V^T P^T of row tile 0 | probabilities of row tile 1
+    //   D  O^T += V^T P^T of row tile 1
+    // A row tile whose packed float16 row sum overflows is re-anchored between phases.
+    for (int it = 0; it < nit; ++it) {
+        const int kb = kbn;
+        const bool more = it + 1 < nit;
+        const bool tail = (kb + 1) * 64 > a.L;
+        kbn = more ? scalar_load(a.col_idx, e0 + it + 1) : 0;
+
+        wait_vmcnt<0>();                          // K(it) and V(it) have landed
+        u32x4 vf[C::NDT][4];
+        {
+            u32x4 kf[2][C::NS];                   // A operand: K[64 kb + 32 kt + n][16 s + 8 h .. +7]
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            f32x16 sacc[2];
+            for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                sacc[kt] = f32x16{};
+                for (int s = 0; s < C::NS; ++s) kf[kt][s] = frag(kslot, 32 * kt + n, 2 * s + h);
+            u32x2 vr[C::NDT][4][2];               // raw bfloat16 V^T fragments
 #pragma unroll
-                for (int s = 0; s < C::NS; ++s)
-                    sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, kf[kt][s]), __builtin_bit_cast(bf16x8, qf[rt][s]), sacc[kt], 0, 0, 0);
-            }
-            if (rt == 1 && more) {
-                // the K fragments are in registers: refill the K slot with the next key block
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                load_k(kbn * 64, 0);
-            }
-            if (tail) {
-                int lim = a.L - kb * 64 - 4 * h;   // keys at local index >= lim do not exist
-                asm volatile("" : "+v"(lim));      // keeps the compares inside this rarely taken branch
+            for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int j = 0; j < 16; ++j)
-                        if (kt * 32 + 8 * (j >> 2) + (j & 3) >= lim) sacc[kt][j] = -INFINITY;
-            }
-            float bsum;
-            auto make_p = [&]() {
-                float sum = 0.f;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const f32x16& sp = sacc[t >> 1];
-                    const int o8 = 8 * (t & 1);
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        const float p0 = fast_exp2(fmaf(sp[o8 + 2 * w], a.c, -mref[rt]));
-                        const float p1 = fast_exp2(fmaf(sp[o8 + 2 * w + 1], a.c, -mref[rt]));
-                        pf[rt][t][w] = pack_f16(p0, p1);
-                        sum = dot2_f16(pf[rt][t][w], sum);
-                    }
+                for (int dt = 0; dt < C::NDT; ++dt) {
+                    const int c = 4 * dt + 2 * (g & 1) + ((s16 & 3) >> 1);
+                    const uint16_t* p = vslot + vrow + 16 * t * C::RS + ((c ^ fv) << 3) + ((s16 & 1) << 2);
+                    vr[dt][t][0] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)p));
+                    vr[dt][t][1] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(p + 8 * C::RS)));
                 }
-                bsum = sum;
-            };
-            make_p();
-            if (__builtin_amdgcn_ballot_w64(!(bsum <= 16384.f)) != 0) {
-                // re-anchor the reference at the true running max and redo this tile
-                float bm = -INFINITY;
+            // phase A
 #pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < 2; ++kt) sacc[0][kt] = sacc[1][kt] = f32x16{};
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) bm = fmaxf(bm, sacc[kt][j]);
-                bm = xhalf_max(bm) * a.c;
-                const float mnew = fmaxf(mref[rt], bm);
-                const float alpha = fast_exp2(mref[rt] - mnew);
-                mref[rt] = mnew;
-                dsum[rt] *= alpha;
+            for (int mi = 0; mi < NA; ++mi) {
+                const int s = mi >> 1, kt = mi & 1;
+                sacc[0][kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, kf[kt][s]), __builtin_bit_cast(bf16x8, qf[0][s]), sacc[0][kt], 0, 0, 0);
 #pragma unroll
-                for (int dt = 0; dt < C::NDT; ++dt) acc[dt][rt] *= alpha;
-                make_p();
+                for (int x = 0; x < VA; ++x) {
+                    const int f = mi * VA + x, dt = f >> 4, t = (f >> 2) & 3, w = f & 3;
+                    vf[dt][t][w] = f16x2_from_bf16x2(vr[dt][t][w >> 1][w & 1]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            dsum[rt] += bsum;
-        }
-
-        // V(it) has landed once at most the K(it+1) refill is still in flight
-        if (more) wait_vmcnt<C::NL>();
-        else wait_vmcnt<0>();
+            // The K and V slots have been read into registers: refill them.  (The empty
+            // statement keeps the re-encoding in this phase instead of next to its use.)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+            for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
-            for (int dt = 0; dt < C::NDT; ++dt) {
-                const int c = 4 * dt + 2 * (g & 1) + ((s16 & 3) >> 1);
-                const uint16_t* p = vslot + vrow + 16 * t * C::RS + ((c ^ fv) << 3) + ((s16 & 1) << 2);
-                const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)p);
-                const i16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(p + 8 * C::RS));
-                const u32x2 w1 = __builtin_bit_cast(u32x2, r1), w2 = __builtin_bit_cast(u32x2, r2);
-                u32x4 vw;
-                vw[0] = f16x2_from_bf16x2(w1[0]);
-                vw[1] = f16x2_from_bf16x2(w1[1]);
-                vw[2] = f16x2_from_bf16x2(w2[0]);
-                vw[3] = f16x2_from_bf16x2(w2[1]);
+                for (int t = 0; t < 4; ++t) asm volatile("" : "+v"(vf[dt][t]));
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (more) {
+                load_k(kbn * 64);
+                load_v(kbn * 64);
+            } else {
+                load_r(q0);
+            }
+            if (__builtin_expect(tail, 0)) mask_tail(0, kb);
+            // phase B
+            bsum[0] = bsum[1] = 0.f;
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
-                    acc[dt][rt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                        __builtin_bit_cast(f16x8, vw), __builtin_bit_cast(f16x8, pf[rt][t]), acc[dt][rt], 0, 0, 0);
+            for (int mi = 0; mi < NA; ++mi) {
+                const int s = mi >> 1, kt = mi & 1;
+                sacc[1][kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, kf[kt][s]), __builtin_bit_cast(bf16x8, qf[1][s]), sacc[1][kt], 0, 0, 0);
+                make_p(0, mi * PB, (mi + 1) * PB);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // the V fragments are read: refill the V slot with the next key block
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if (more) load_v(kbn * 64, 1);
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(bsum[0] <= 16384.f)) != 0, 0)) reanchor(0);
+        dsum[0] += bsum[0];
+        if (__builtin_expect(tail, 0)) mask_tail(1, kb);
+        // phase C
+#pragma unroll
+        for (int mi = 0; mi < NC; ++mi) {
+            const int t = mi / C::NDT, dt = mi % C::NDT;
+            acc[dt][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                __builtin_bit_cast(f16x8, vf[dt][t]), __builtin_bit_cast(f16x8, pf[0][t]), acc[dt][0], 0, 0, 0);
+            make_p(1, mi * PC, (mi + 1) * PC);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(bsum[1] <= 16384.f)) != 0, 0)) reanchor(1);
+        dsum[1] += bsum[1];
+        // phase D
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt)
+                acc[dt][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                    __builtin_bit_cast(f16x8, vf[dt][t]), __builtin_bit_cast(f16x8, pf[1][t]), acc[dt][1], 0, 0, 0);
     }
 
     // Epilogue: O' = min(1, rho * ramp) * acc / D' + R, transposed through LDS so
     // that R is read and O written as whole 128-byte rows.
-    wait_vmcnt<0>();
-    load_r(q0, 1);
     float scale[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
-        const int row = q0 + 32 * rt + n;
-        const float rho = row < a.L ? a.rho_in[(int64_t)bh * a.L + row] : 0.f;
         const float dtot = xhalf_sum(dsum[rt]);
-        scale[rt] = nit > 0 ? fminf(1.f, rho * a.ramp) / dtot : 0.f;
+        scale[rt] = nit > 0 ? fminf(1.f, rho_r[rt] * a.ramp) / dtot : 0.f;
     }
-    wait_vmcnt<0>();
+    wait_vmcnt<0>();                          // R has landed in the V slot
     // lane (n, h) owns d = 32 dt + 8 bb + 4 h + r of rows 32 rt + n: read R there, write O there
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
