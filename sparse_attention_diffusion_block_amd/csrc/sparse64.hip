@@ -23,10 +23,10 @@
 //   * P*V runs in float16 (P rounds 8x finer than in bfloat16); V is
 //     re-encoded exactly as its fragments are read;
 //   * the softmax keeps a running reference per row instead of a per-block
-//     max: a block's probabilities are computed against the current
-//     reference, and only if a row's packed float16 sum is non-finite or
-//     above 2^14 is the block redone against its true max (rescaling the
-//     accumulators).  Any reference gives the same mathematics; the bound
+//     max: the first kept block sets it to its row max, later blocks'
+//     probabilities are computed against it, and only if a row's packed
+//     float16 sum is non-finite or above 2^14 is the block redone against
+//     its true max (rescaling the accumulators).  Any reference gives the same mathematics; the bound
 //     keeps every float16 probability finite.
 #include "attn.h"
 #include "common.h"
@@ -93,14 +93,15 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)a.R_in + base), 0, nrec, 0x00020000);
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc((void*)((uint16_t*)a.O + base), 0, nrec, 0x00020000);
 
-    // lane -> (row within an 8-row group, physical chunk) of a tile transfer
+    // lane -> (row within an 8-row group, physical chunk) of a tile transfer.  Row 8 i + trow
+    // has the same swizzle as row trow, so a lane's byte offset within every 8-row group is
+    // a constant; the group's row offset goes in the scalar offset.  Both offsets count in
+    // the buffer range check, so rows at or past L read as zero (and stores to them are
+    // dropped), and a padded chunk (d <= 16 c) takes an offset past every record.
     const int trow = lane >> 3, tpc = lane & 7;
-    // (select by arithmetic, not by a conditional: a conditional offset here is turned
-    // into exec-masked branches around the transfer)
-#define RETTN_TILE_OFF(ROW0, I)                                                                        \
-    ((((uint32_t)((ROW0) + 8 * (I) + trow) * row_bytes + 16u * (uint32_t)(tpc ^ swz(8 * (I) + trow))) & \
-      (0u - (uint32_t)((tpc ^ swz(8 * (I) + trow)) * 8 < a.d))) |                                          \
-     (kOOB & ((uint32_t)((tpc ^ swz(8 * (I) + trow)) * 8 < a.d) - 1u)))
+    const uint32_t lane_off = (tpc ^ swz(trow)) * 8 < a.d
+                                  ? (uint32_t)trow * row_bytes + 16u * (uint32_t)(tpc ^ swz(trow)) : kOOB;
+#define RETTN_ROW_OFF(ROW0, I) ((uint32_t)((ROW0) + 8 * (I)) * row_bytes)
     // (plain expressions only inside these loaders: a lambda called from another
     // lambda here, a buffer-resource lambda parameter or a generic pointer cast to
     // the LDS address space keeps the host compiler from emitting the launch stub)
@@ -108,7 +109,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     auto NAME = [&](int row0) {                                                                                  \
         _Pragma("unroll") for (int i = 0; i < C::NL; ++i)                                                         \
             __builtin_amdgcn_raw_ptr_buffer_load_lds(RSRC, (__attribute__((address_space(3))) void*)(SLOT + i * 512), \
-                                                     16, RETTN_TILE_OFF(row0, i), 0, 0, 0);                      \
+                                                     16, lane_off, RETTN_ROW_OFF(row0, i), 0, 0);               \
     };
     RETTN_TILE_LOADER(load_q, rq, vslot)
     RETTN_TILE_LOADER(load_k, rk, kslot)
@@ -152,8 +153,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     f32x16 acc[C::NDT][2];
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt) acc[dt][0] = acc[dt][1] = f32x16{};
-    // Running reference per row, log2 units.  It starts at -inf, so the first kept
-    // block always takes the re-anchoring path below and anchors at its own max.
+    // Running reference per row, log2 units: the max of the row's first kept block, raised
+    // only when a later block would overflow the float16 probabilities.
     float mref[2] = {-INFINITY, -INFINITY};
     float dsum[2] = {0.f, 0.f};
 
@@ -180,16 +181,21 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             bsum[rt] = dot2_f16(pf[rt][t][w], bsum[rt]);
         }
     };
+    // max of the current block's scores over each row of row tile rt, log2 units
+    auto row_max = [&](int rt) -> float {
+        float m[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) m[j] = fmaxf(sacc[rt][0][j], sacc[rt][1][j]);
+#pragma unroll
+        for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+            for (int j = 0; j < w; ++j) m[j] = fmaxf(m[j], m[j + w]);
+        return xhalf_max(m[0]) * a.c;
+    };
     // re-anchor the reference of row tile rt at the true running max (rescaling what is
     // accumulated), then redo its probabilities
     auto reanchor = [&](int rt) {
-        float bm = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) bm = fmaxf(bm, sacc[rt][kt][j]);
-        bm = xhalf_max(bm) * a.c;
-        const float mnew = fmaxf(mref[rt], bm);
+        const float mnew = fmaxf(mref[rt], row_max(rt));
         const float alpha = fast_exp2(mref[rt] - mnew);
         mref[rt] = mnew;
         dsum[rt] *= alpha;
@@ -279,6 +285,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 load_r(q0);
             }
             if (__builtin_expect(tail, 0)) mask_tail(0, kb);
+            if (it == 0) mref[0] = row_max(0);    // first kept block: nothing accumulated yet
             // phase B
             bsum[0] = bsum[1] = 0.f;
 #pragma unroll
@@ -293,6 +300,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(bsum[0] <= 16384.f)) != 0, 0)) reanchor(0);
         dsum[0] += bsum[0];
         if (__builtin_expect(tail, 0)) mask_tail(1, kb);
+        if (it == 0) mref[1] = row_max(1);
         // phase C
 #pragma unroll
         for (int mi = 0; mi < NC; ++mi) {
@@ -344,9 +352,9 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
     for (int i = 0; i < C::NL; ++i) {
         const u32x4 w = *(const u32x4*)(vslot + (8 * i + trow) * C::RS + tpc * 8);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), ro, RETTN_TILE_OFF(q0, i), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), ro, lane_off, RETTN_ROW_OFF(q0, i), 0);
     }
-#undef RETTN_TILE_OFF
+#undef RETTN_ROW_OFF
 }
 
 template <int DP>
