@@ -16,7 +16,7 @@ import pytest
 import oracle
 from oracle import masks as om
 from tests.gpu_util import assert_parity, dev, host, log
-from workloads import CONFIGS, MaskSpec, bf16_round, drift, make_cache, make_qkv, random_mask, sample_rows
+from workloads import CONFIGS, SWEEP_C3, MaskSpec, bf16_round, drift, make_cache, make_qkv, random_mask, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -222,3 +222,36 @@ def _full_config(rt, n, nrows):
 @pytest.mark.parametrize("n,nrows", [(1, 1024), (2, 96), (3, 48), (4, 96), (5, 12)])
 def test_full_size_config(rt, n, nrows):
     _full_config(rt, n, nrows)
+
+
+# ------------------------------------------------------------------ density sweep on the video workload's shapes
+@pytest.mark.timeout(900)
+def test_sparsity_sweep_c3_shapes(rt):
+    """Band windows of 75 / 87.5 / 93.8 / 96.9% block sparsity at B=2, H=30, L=17776, d=64 (sampled rows)."""
+    import torch
+    cfg = CONFIGS[3]
+    q, k, v = make_qkv(cfg.B, cfg.H, cfg.L, cfg.d, cfg.seed, dtype=cfg.dtype)
+    q2, k2, v2 = drift(q, k, v, cfg.number, 1, sigma=cfg.drift_sigma, dtype=cfg.dtype)
+    rows = sample_rows(cfg.L, cfg.block, 24, seed=33)
+    rho_c, r_c = make_cache(cfg.B, cfg.H, cfg.L, cfg.d, seed=33, dtype=cfg.dtype)
+    tq, tk, tv = (dev(x, cfg.dtype) for x in (q, k, v))
+    tq2, tk2, tv2 = (dev(x, cfg.dtype) for x in (q2, k2, v2))
+    trho, tr = torch.from_numpy(rho_c).cuda(), dev(r_c, cfg.dtype)
+    for spec in SWEEP_C3:
+        log(f" mask {spec.label()}")
+        mask = om.build_mask(spec.kind, spec.nb, spec.w)
+        assert int(mask.sum(axis=1).min()) == int(mask.sum(axis=1).max()) == spec.w
+        idx = rt.index_build(rt.mask_build(spec.kind, spec.nb, spec.w), cfg.block)
+        o_g, rho_g, r_g = rt.calibrate(tq, tk, tv, idx)
+        torch.cuda.synchronize()
+        o_o, rho_o, r_o = oracle.calibrate(q, k, v, mask, cfg.block, rows=rows)
+        assert_parity(host(o_g[:, :, rows]), o_o, cfg.dtype, "calibrate O")
+        assert_parity(host(rho_g[:, :, rows]), rho_o, cfg.dtype, "calibrate rho")
+        assert_parity(host(r_g[:, :, rows]), r_o, cfg.dtype, "calibrate R")
+        del o_g, rho_g, r_g
+        o2_g = rt.sparse(tq2, tk2, tv2, idx, trho, tr, lam=cfg.lam, step=2)
+        torch.cuda.synchronize()
+        o2_o = oracle.sparse_step(q2, k2, v2, mask, cfg.block, rho_c[:, :, rows], r_c[:, :, rows], cfg.lam, 2,
+                                  rows=rows)
+        assert_parity(host(o2_g[:, :, rows]), o2_o, cfg.dtype, "sparse O'")
+        del o2_g

@@ -6,10 +6,10 @@ draws.  It contains none of the attention method's arithmetic, so both the
 CPU oracle and the GPU path can take their inputs from it without sharing
 any computation.
 """
-from .configs import CONFIGS, MaskSpec, Config, MASK_DIAG, MASK_BAND, MASK_COGVIDEO3D, MASK_FULL, MASK_CUSTOM
+from .configs import CONFIGS, SWEEP_C3, MaskSpec, Config, MASK_DIAG, MASK_BAND, MASK_COGVIDEO3D, MASK_FULL, MASK_CUSTOM
 from .gen import bf16_round, make_qkv, drift, sample_rows, make_cache, random_mask
 
 __all__ = [
-    "CONFIGS", "MaskSpec", "Config", "MASK_DIAG", "MASK_BAND", "MASK_COGVIDEO3D", "MASK_FULL", "MASK_CUSTOM",
+    "CONFIGS", "SWEEP_C3", "MaskSpec", "Config", "MASK_DIAG", "MASK_BAND", "MASK_COGVIDEO3D", "MASK_FULL", "MASK_CUSTOM",
     "bf16_round", "make_qkv", "drift", "sample_rows", "make_cache", "random_mask",
 ]

@@ -84,3 +84,7 @@ def _cfgs() -> dict:
 
 
 CONFIGS = _cfgs()
+
+# Density sweep on the shapes of workload 3: band windows of round-half-up(278 * {1/4, 1/8, 1/16,
+# 1/32}) key blocks per query block, i.e. 75 / 87.5 / 93.8 / 96.9% nominal block sparsity.
+SWEEP_C3 = tuple(MaskSpec(MASK_BAND, 278, w=w) for w in (70, 35, 17, 9))
