@@ -127,6 +127,27 @@ rettn_status rettn_calibrate(const rettn_desc* desc, const void* Q, const void* 
                              const rettn_index* idx, void* O, float* rho, void* R,
                              hipStream_t stream);
 
+/* Which residual a calibration writes into R. */
+typedef enum {
+    /* Re-ttention's residual: the masked keys' share of full attention,
+     * R_i = sum_{j not in W(i)} e^{s_j} v_j / sum_j e^{s_j}. */
+    RETTN_RESIDUAL_MASKED = 0,
+    /* The DiTFastAttn comparator's residual: full attention minus window
+     * attention, R_i = O_i - softmax_{W(i)}(s) V_{W(i)} (O_i when W(i) is
+     * empty); its later steps add it to plain window attention (review
+     * thread, reply to W1 of the first review, on how the two residuals
+     * differ). */
+    RETTN_RESIDUAL_DIFFERENCE = 1
+} rettn_residual;
+
+/* rettn_calibrate with a choice of residual: identical O and rho; R as
+ * `kind` says, computed from the float32 accumulators and rounded once to
+ * the I/O type.  rettn_calibrate is this call with RETTN_RESIDUAL_MASKED.
+ * An unknown `kind` gives RETTN_EINVAL with nothing launched. */
+rettn_status rettn_calibrate_residual(const rettn_desc* desc, const void* Q, const void* K, const void* V,
+                                      const rettn_index* idx, void* O, float* rho, void* R,
+                                      rettn_residual kind, hipStream_t stream);
+
 /* Sparse step `step` (>= 1 sparse steps since the last calibration):
  *   O'_i = min(1, rho_i (1 + lambda step)) * softmax_{W(i)}(s') V'_{W(i)} + R_i
  * over the kept key blocks only (review thread, replies to W1 of the first

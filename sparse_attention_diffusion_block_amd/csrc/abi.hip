@@ -141,6 +141,13 @@ rettn_status rettn_index_build(const uint8_t* mask_dev, int32_t nqb, int32_t nkb
 
 rettn_status rettn_calibrate(const rettn_desc* desc, const void* Q, const void* K, const void* V,
                              const rettn_index* idx, void* O, float* rho, void* R, hipStream_t stream) {
+    return rettn_calibrate_residual(desc, Q, K, V, idx, O, rho, R, RETTN_RESIDUAL_MASKED, stream);
+}
+
+rettn_status rettn_calibrate_residual(const rettn_desc* desc, const void* Q, const void* K, const void* V,
+                                      const rettn_index* idx, void* O, float* rho, void* R, rettn_residual kind,
+                                      hipStream_t stream) {
+    if (kind != RETTN_RESIDUAL_MASKED && kind != RETTN_RESIDUAL_DIFFERENCE) return RETTN_EINVAL;
     rettn_status st = check_desc(desc, idx);
     if (st != RETTN_OK) return st;
     st = check_tensors({Q, K, V, O, R});
@@ -151,6 +158,7 @@ rettn_status rettn_calibrate(const rettn_desc* desc, const void* Q, const void* 
     AttnArgs a = make_args(desc, Q, K, V, idx, O);
     a.R_out = R;
     a.rho_out = rho;
+    a.residual = kind == RETTN_RESIDUAL_DIFFERENCE ? 1 : 0;
     const hipError_t e = desc->dtype == RETTN_BF16 ? rettn::launch_calibrate_bf16(a, desc->block, stream)
                                                    : rettn::launch_calibrate_f32(a, desc->block, stream);
     return e == hipSuccess ? RETTN_OK : RETTN_EHIP;

@@ -25,6 +25,8 @@ struct AttnArgs {
     float c;                  // log2(e) / sqrt(d): scores enter exp2 pre-scaled
     float ramp;               // 1 + lambda * step (sparse step only)
     int32_t G;                // work-groups in the launch
+    int32_t residual;         // calibration's R: 0 masked keys' share of O (Re-ttention), 1 full minus window
+                              // attention (the DiTFastAttn comparator)
 };
 
 // d is padded to DP in {32, 64, 96, 128} inside the kernels.

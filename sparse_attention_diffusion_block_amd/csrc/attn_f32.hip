@@ -225,6 +225,9 @@ attn_f32_kernel(const AttnArgs a) {
     if constexpr (CALIB) {
         const float din = xhalf_sum(dsum), dout = xhalf_sum(dsum2);
         const float inv = 1.f / (din + dout);
+        // window attention's normaliser for the difference residual (no kept key: the window output is 0)
+        const float inv_in = din > 0.f ? 1.f / din : 0.f;
+        const bool diff = a.residual != 0;
         if (row_ok && h == 0) a.rho_out[(int64_t)bh * a.L + row] = din * inv;
         float* Rp = (float*)a.R_out + base + (int64_t)row * a.sl;
 #pragma unroll
@@ -236,8 +239,9 @@ attn_f32_kernel(const AttnArgs a) {
                     f32x4 ov, rv;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        ov[r] = (acc[dt][4 * bb + r] + acc2[dt][4 * bb + r]) * inv;
-                        rv[r] = acc2[dt][4 * bb + r] * inv;
+                        const float ai = acc[dt][4 * bb + r], ao = acc2[dt][4 * bb + r];
+                        ov[r] = (ai + ao) * inv;
+                        rv[r] = diff ? ov[r] - ai * inv_in : ao * inv;
                     }
                     *(f32x4*)(Op + d0) = ov;
                     *(f32x4*)(Rp + d0) = rv;

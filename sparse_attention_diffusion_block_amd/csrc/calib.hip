@@ -247,6 +247,9 @@ __global__ void __launch_bounds__(512) calib_kernel(const AttnArgs a) {
     // Epilogue.  Lane (n, h) owns d = 32 dt + 8 bb + 4 h + r of row `row`.
     const float din = xhalf_sum(d_in), dout = xhalf_sum(d_out);
     const float inv = 1.f / (din + dout);
+    // window attention's normaliser for the difference residual (no kept key: the window output is 0)
+    const float inv_in = din > 0.f ? 1.f / din : 0.f;
+    const bool diff = a.residual != 0;
     if (row_ok && h == 0) a.rho_out[(int64_t)bh * a.L + row] = din * inv;
     uint16_t* Op = (uint16_t*)a.O + base + (int64_t)row * a.sl;
     uint16_t* Rp = (uint16_t*)a.R_out + base + (int64_t)row * a.sl;
@@ -256,12 +259,18 @@ __global__ void __launch_bounds__(512) calib_kernel(const AttnArgs a) {
         for (int bb = 0; bb < 4; ++bb) {
             const int d0 = 32 * dt + 8 * bb + 4 * h;
             if (row_ok && d0 < a.d) {
-                const int j = 4 * bb;
+                float ov[4], rv[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float ai = acc_in[dt][4 * bb + r], ao = acc_out[dt][4 * bb + r];
+                    ov[r] = (ai + ao) * inv;
+                    rv[r] = diff ? ov[r] - ai * inv_in : ao * inv;
+                }
                 u32x2 ow, rw;
-                ow[0] = pack_bf16((acc_in[dt][j] + acc_out[dt][j]) * inv, (acc_in[dt][j + 1] + acc_out[dt][j + 1]) * inv);
-                ow[1] = pack_bf16((acc_in[dt][j + 2] + acc_out[dt][j + 2]) * inv, (acc_in[dt][j + 3] + acc_out[dt][j + 3]) * inv);
-                rw[0] = pack_bf16(acc_out[dt][j] * inv, acc_out[dt][j + 1] * inv);
-                rw[1] = pack_bf16(acc_out[dt][j + 2] * inv, acc_out[dt][j + 3] * inv);
+                ow[0] = pack_bf16(ov[0], ov[1]);
+                ow[1] = pack_bf16(ov[2], ov[3]);
+                rw[0] = pack_bf16(rv[0], rv[1]);
+                rw[1] = pack_bf16(rv[2], rv[3]);
                 *(u32x2*)(Op + d0) = ow;
                 *(u32x2*)(Rp + d0) = rw;
             }

@@ -14,7 +14,9 @@ LIB_PATH = os.path.join(_HERE, "librettn.so")
 
 RETTN_F32, RETTN_BF16 = 0, 1
 MASK_DIAG, MASK_BAND, MASK_COGVIDEO3D, MASK_FULL = 0, 1, 2, 3
-EXPORTED = ("rettn_mask_build", "rettn_index_build", "rettn_calibrate", "rettn_sparse", "rettn_status_str")
+RESIDUAL_MASKED, RESIDUAL_DIFFERENCE = 0, 1
+EXPORTED = ("rettn_mask_build", "rettn_index_build", "rettn_calibrate", "rettn_calibrate_residual", "rettn_sparse",
+            "rettn_status_str")
 
 
 class Desc(ctypes.Structure):
@@ -48,6 +50,10 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built; run sparse_attention_diffusion_block_amd.build.build()")
+        # torch first: it loads the HIP runtime it ships with, and the library must bind to that
+        # same runtime (loaded first, the library would pull in the system one, whose streams and
+        # allocations are foreign to torch's)
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         vp, i32 = ctypes.c_void_p, ctypes.c_int32
         L.rettn_status_str.argtypes = [ctypes.c_int]
@@ -58,6 +64,9 @@ def lib():
         L.rettn_index_build.restype = ctypes.c_int
         L.rettn_calibrate.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, ctypes.POINTER(Index), vp, vp, vp, vp]
         L.rettn_calibrate.restype = ctypes.c_int
+        L.rettn_calibrate_residual.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, ctypes.POINTER(Index), vp, vp, vp,
+                                               ctypes.c_int, vp]
+        L.rettn_calibrate_residual.restype = ctypes.c_int
         L.rettn_sparse.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, ctypes.POINTER(Index), vp, vp,
                                    ctypes.c_float, i32, vp, vp]
         L.rettn_sparse.restype = ctypes.c_int
@@ -137,8 +146,11 @@ def _desc(t, block):
     return Desc(B, H, L, d, block, _dtype_code(t), sb, sh, sl)
 
 
-def calibrate(q, k, v, index, out=None):
-    """Full-attention calibration step -> (O, rho, R).  O and R have q's dtype; rho is float32 [B,H,L]."""
+def calibrate(q, k, v, index, out=None, residual="masked"):
+    """Full-attention calibration step -> (O, rho, R).  O and R have q's dtype; rho is float32 [B,H,L].
+
+    residual="masked" gives Re-ttention's R (the masked keys' share of O); "difference" gives
+    the DiTFastAttn comparator's residual (full minus window attention)."""
     import torch
     q, k, v = _prep((q, k, v))
     B, H, L, d = q.shape
@@ -150,8 +162,10 @@ def calibrate(q, k, v, index, out=None):
         o, rho, r = out
     desc = _desc(q, index.block)
     idx = index.c_struct()
-    _check(lib().rettn_calibrate(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(idx),
-                                 o.data_ptr(), rho.data_ptr(), r.data_ptr(), _stream(q.device)), "rettn_calibrate")
+    kind = {"masked": RESIDUAL_MASKED, "difference": RESIDUAL_DIFFERENCE}[residual]
+    _check(lib().rettn_calibrate_residual(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                          ctypes.byref(idx), o.data_ptr(), rho.data_ptr(), r.data_ptr(), kind,
+                                          _stream(q.device)), "rettn_calibrate_residual")
     return o, rho, r
 
 

@@ -129,3 +129,17 @@ def test_index_build_rejects_bad_arguments():
     assert lib.rettn_index_build(FAKE, 0, 4, FAKE, FAKE, ctypes.byref(nnz), None) == EINVAL
     assert lib.rettn_index_build(FAKE, 4, 4, FAKE, FAKE, None, None) == EINVAL
     assert nnz.value == -1
+
+
+@pytest.mark.parametrize("kind", [-1, 2, 99])
+def test_calibrate_residual_rejects_unknown_kind(kind):
+    lib = rt.lib()
+    d = _good_desc()
+    idx = _idx()
+    assert lib.rettn_calibrate_residual(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(idx), FAKE, FAKE, FAKE,
+                                        kind, None) == EINVAL
+    # a bad descriptor is rejected for either valid kind too
+    d.d = 0
+    for good in (b.RESIDUAL_MASKED, b.RESIDUAL_DIFFERENCE):
+        assert lib.rettn_calibrate_residual(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(idx), FAKE, FAKE, FAKE,
+                                            good, None) == EINVAL
