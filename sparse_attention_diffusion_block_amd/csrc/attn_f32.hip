@@ -193,7 +193,7 @@ attn_f32_kernel(const AttnArgs a) {
         dsum *= alpha;
         dsum2 *= alpha;
         bool in_window = true;
-        if constexpr (CALIB) in_window = scalar_load(a.mask, mrow + kb) != 0;
+        if constexpr (CALIB) in_window = mask_byte(a.mask, mrow + kb) != 0;
         if (in_window) dsum += psum;
         else dsum2 += psum;
 

@@ -213,7 +213,7 @@ __global__ void __launch_bounds__(512) calib_kernel(const AttnArgs a) {
             make_p();
         }
 
-        const bool in_window = scalar_load(a.mask, mrow + (kt64 * 64) / BLOCK) != 0;
+        const bool in_window = mask_byte(a.mask, mrow + (kt64 * 64) / BLOCK) != 0;
         auto pv = [&](f32x16 (&dst)[C::NDT]) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) {

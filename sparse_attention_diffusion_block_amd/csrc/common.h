@@ -58,9 +58,20 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // which are counted by lgkmcnt, so waiting for them never drains the vector
 // loads (K/V prefetches) that are in flight.
 typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
-typedef const __attribute__((address_space(4))) uint8_t* const_u8_ptr;
+typedef const __attribute__((address_space(4))) uint32_t* const_u32_ptr;
 __device__ __forceinline__ int32_t scalar_load(const int32_t* p, int64_t i) { return ((const_i32_ptr)p)[i]; }
-__device__ __forceinline__ uint8_t scalar_load(const uint8_t* p, int64_t i) { return ((const_u8_ptr)p)[i]; }
+
+// One mask byte, wave-uniform.  gfx950 has no scalar byte load: a byte read
+// through the constant address space becomes a vector load, and its wait
+// (vmcnt) would drain every prefetch issued before it.  So the aligned dword
+// holding the byte is read with a scalar load and the byte shifted out.  That
+// dword never crosses a page, so its other bytes (possibly just outside the
+// mask) are always mapped; they are discarded.
+__device__ __forceinline__ uint32_t mask_byte(const uint8_t* p, int64_t i) {
+    const uintptr_t addr = (uintptr_t)(p + i);
+    const uint32_t w = *(const_u32_ptr)(addr & ~(uintptr_t)3);
+    return (w >> (8u * (uint32_t)(addr & 3u))) & 0xffu;
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
