@@ -9,11 +9,13 @@ row block or one (batch, head) at a time, so a reader can check it against
 the pages by eye.
 """
 from .masks import diag_mask, band_mask, cogvideo3d_mask, full_mask, build_mask, csr_from_mask, mask_density
-from .rettn import (tau, ramp, key_keep, calibrate, sparse_step, full_attention, window_attention,
+from .dynamic import block_means, block_scores, dynamic_mask
+from .rettn import (tau, ramp, key_keep, slice_mask, calibrate, sparse_step, full_attention, window_attention,
                     ditfastattn_residual, ditfastattn_step, post_softmax_masked, textbook_attention)
 
 __all__ = [
     "diag_mask", "band_mask", "cogvideo3d_mask", "full_mask", "build_mask", "csr_from_mask", "mask_density",
-    "tau", "ramp", "key_keep", "calibrate", "sparse_step", "full_attention", "window_attention",
+    "block_means", "block_scores", "dynamic_mask",
+    "tau", "ramp", "key_keep", "slice_mask", "calibrate", "sparse_step", "full_attention", "window_attention",
     "ditfastattn_residual", "ditfastattn_step", "post_softmax_masked", "textbook_attention",
 ]

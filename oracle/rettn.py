@@ -28,6 +28,8 @@ Readings where the pages are silent (each is listed in the design notes):
     lambda = 0 (no formula is printed); pinned only by internal algebra.
   * Softmax scale tau = 1/sqrt(d) with the true head dimension.
   * Keys at positions >= L do not exist; an empty window gives O' = R.
+  * Every `mask` argument may be one block mask shared by all (batch, head)
+    slices or one mask per head or per slice (see slice_mask).
 """
 import math
 
@@ -48,6 +50,27 @@ def key_keep(mask, block, L, qb):
     """Token-level kept keys of query block qb: key j is kept iff mask[qb, j // block] != 0."""
     blocks = np.arange(L) // block
     return np.asarray(mask)[qb, blocks] != 0
+
+
+def slice_mask(mask, b, h, B, H):
+    """The block mask that (batch b, head h) uses.
+
+    A 2-D mask [nqb, nkb] is shared by every (b, h).  A 3-D mask [S, nqb, nkb]
+    holds one mask per slice: S = 1 shared, S = H one per head (the same for
+    every batch element), S = B*H one per (b, h) in the order b*H + h.  Heads
+    keep their own statistics (review thread, answer to Q2 of the first
+    review), so nothing ties one head's window to another's."""
+    mask = np.asarray(mask)
+    if mask.ndim == 2:
+        return mask
+    S = mask.shape[0]
+    if S == 1:
+        return mask[0]
+    if S == B * H:
+        return mask[b * H + h]
+    if S == H:
+        return mask[h]
+    raise ValueError(f"a mask of {S} slices fits neither 1, H = {H} nor B*H = {B * H}")
 
 
 def _rows_by_block(rows, block):
@@ -84,8 +107,9 @@ def calibrate(q, k, v, mask, block, rows=None):
     groups = _rows_by_block(rows, block)
     for b in range(B):
         for h in range(H):
+            m_bh = slice_mask(mask, b, h, B, H)
             for qb, pos in groups.items():
-                keep = key_keep(mask, block, L, qb)
+                keep = key_keep(m_bh, block, L, qb)
                 qi = q[b, h, rows[pos]]
                 s = t * (qi @ k[b, h].T)
                 m = s.max(axis=1, keepdims=True)
@@ -112,8 +136,9 @@ def window_attention(q, k, v, mask, block, rows=None):
     groups = _rows_by_block(rows, block)
     for b in range(B):
         for h in range(H):
+            m_bh = slice_mask(mask, b, h, B, H)
             for qb, pos in groups.items():
-                keep = key_keep(mask, block, L, qb)
+                keep = key_keep(m_bh, block, L, qb)
                 if not keep.any():
                     continue
                 kk, vv = k[b, h][keep], v[b, h][keep]
@@ -136,10 +161,14 @@ def sparse_step(q, k, v, mask, block, rho, r, lam, step, rows=None):
     o_sp = window_attention(q, k, v, mask, block, rows)
     rho = _as64(rho)
     r = _as64(r)
-    L = np.asarray(q).shape[2]
+    B, H, L, _ = np.asarray(q).shape
     rows_arr = np.arange(L) if rows is None else np.asarray(rows, dtype=np.int64)
-    nonempty = np.array([bool(np.asarray(mask)[int(i) // block].any()) for i in rows_arr])
-    scale = ramp(rho, lam, step) * nonempty[None, None, :]
+    nonempty = np.zeros((B, H, len(rows_arr)))
+    for b in range(B):
+        for h in range(H):
+            m_bh = slice_mask(mask, b, h, B, H)
+            nonempty[b, h] = [bool(m_bh[int(i) // block].any()) for i in rows_arr]
+    scale = ramp(rho, lam, step) * nonempty
     return scale[..., None] * o_sp + r
 
 
@@ -203,8 +232,9 @@ def post_softmax_masked(q, k, v, mask, block, rows=None):
     groups = _rows_by_block(rows, block)
     for b in range(B):
         for h in range(H):
+            m_bh = slice_mask(mask, b, h, B, H)
             for qb, pos in groups.items():
-                keep = key_keep(mask, block, L, qb)
+                keep = key_keep(m_bh, block, L, qb)
                 s = t * (q[b, h, rows[pos]] @ k[b, h].T)
                 e = np.exp(s - s.max(axis=1, keepdims=True))
                 p = e / e.sum(axis=1, keepdims=True)

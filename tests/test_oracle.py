@@ -113,6 +113,36 @@ def test_all_masks_3x3_brute_force():
         np.testing.assert_allclose(out, full, atol=1e-12)
 
 
+def test_per_slice_masks_brute_force():
+    """One mask per head ([H, nb, nb]) and one per (batch, head) ([B*H, nb, nb], order b*H + h):
+    each slice's rho and R follow its own mask, by the token-level definitions; an empty row in
+    one slice gives O' = R in that slice only."""
+    B, H, L, d, block = 2, 3, 5, 3, 2
+    q, k, v = (_rand((B, H, L, d), s) for s in (21, 22, 23))
+    p = softmax(_scores(q, k), axis=-1)
+    blocks = np.arange(L) // block
+    g = np.random.Generator(np.random.PCG64(24))
+    per_slice = (g.random((B * H, 3, 3)) < 0.5).astype(np.uint8)
+    per_slice[4, 1] = 0                                  # slice (1, 1): query block 1 keeps nothing
+    per_head = per_slice[:H].copy()
+    for masks, pick in ((per_slice, lambda b, h: per_slice[b * H + h]), (per_head, lambda b, h: per_head[h])):
+        o, rho, r = oracle.calibrate(q, k, v, masks, block)
+        out = oracle.sparse_step(q, k, v, masks, block, rho, r, lam=0.0, step=1)
+        for b in range(B):
+            for h in range(H):
+                keep = pick(b, h)[blocks][:, blocks] != 0
+                np.testing.assert_allclose(rho[b, h], (p[b, h] * keep).sum(-1), atol=1e-12)
+                np.testing.assert_allclose(r[b, h], (p[b, h] * ~keep) @ v[b, h], atol=1e-12)
+                np.testing.assert_allclose(out[b, h], p[b, h] @ v[b, h], atol=1e-12)
+    # the empty row of slice (1, 1) alone: the ramp cannot touch it, O' = R exactly
+    o, rho, r = oracle.calibrate(q, k, v, per_slice, block)
+    out = oracle.sparse_step(q, k, v, per_slice, block, rho, r, lam=0.5, step=3)
+    np.testing.assert_array_equal(out[1, 1, 2:4], r[1, 1, 2:4])
+    assert np.all(rho[1, 1, 2:4] == 0.0)
+    with pytest.raises(ValueError):
+        oracle.calibrate(q, k, v, per_slice[:4], block)
+
+
 # ---------------------------------------------------------------- invariants
 def _small_case(seed=0, B=2, H=2, L=40, d=8, block=8, density=0.4):
     q, k, v = (_rand((B, H, L, d), seed + s) for s in range(3))

@@ -24,8 +24,10 @@ MUTATIONS = [
     ("sign of the max shift", "e = np.exp(s - m)\n                D = e.sum", "e = np.exp(m - s)\n                D = e.sum"),
     ("scores transposed (k_i . q_j)", "s = t * (qi @ k[b, h].T)", "s = t * (k[b, h][rows[pos]] @ q[b, h].T)"),
     ("value operand transposed", "o[b, h, pos] = (e @ v[b, h])", "o[b, h, pos] = (e @ v[b, h][::-1])"),
-    ("scale uses L instead of d", "t = tau(d)\n    groups = _rows_by_block(rows, block)\n    for b in range(B):\n        for h in range(H):\n            for qb, pos in groups.items():\n                keep = key_keep(mask, block, L, qb)\n                qi",
-     "t = tau(L)\n    groups = _rows_by_block(rows, block)\n    for b in range(B):\n        for h in range(H):\n            for qb, pos in groups.items():\n                keep = key_keep(mask, block, L, qb)\n                qi"),
+    ("scale uses L instead of d", "t = tau(d)\n    groups = _rows_by_block(rows, block)\n    for b in range(B):\n        for h in range(H):\n            m_bh = slice_mask(mask, b, h, B, H)\n            for qb, pos in groups.items():\n                keep = key_keep(m_bh, block, L, qb)\n                qi",
+     "t = tau(L)\n    groups = _rows_by_block(rows, block)\n    for b in range(B):\n        for h in range(H):\n            m_bh = slice_mask(mask, b, h, B, H)\n            for qb, pos in groups.items():\n                keep = key_keep(m_bh, block, L, qb)\n                qi"),
+    ("per-head masks swapped between heads", "        return mask[h]\n", "        return mask[H - 1 - h]\n"),
+    ("per-slice masks indexed head-major", "        return mask[b * H + h]\n", "        return mask[h * B + b]\n"),
     ("residual not added", "return scale[..., None] * o_sp + r", "return scale[..., None] * o_sp"),
     ("ramp applied to the residual", "return scale[..., None] * o_sp + r", "return scale[..., None] * (o_sp + r)"),
     ("ramp sign", "rho * (1.0 + float(lam) * float(step))", "rho * (1.0 - float(lam) * float(step))"),
@@ -56,6 +58,7 @@ def _run_pins(m):
             lambda: pins.test_worked_example_drift(read_golden),
             lambda: pins.test_calibration_is_textbook_attention(1, 2, 7, 4, 3),
             lambda: pins.test_all_masks_3x3_brute_force(),
+            lambda: pins.test_per_slice_masks_brute_force(),
             lambda: pins.test_sum_to_one(),
             lambda: pins.test_reconstruction_on_calibration_inputs(),
             lambda: pins.test_ramp_algebra(),
