@@ -31,6 +31,7 @@
 #ifndef RETTN_H
 #define RETTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -82,14 +83,27 @@ typedef struct {
     int32_t tshift;        /* COGVIDEO3D: temporal offset in blocks, >= 1 */
 } rettn_mask_spec;
 
-/* The compacted static mask, all arrays in device memory and owned by the caller.
+/* The compacted block mask, all arrays in device memory and owned by the caller.
  *   mask     uint8 [nqb * nkb] row-major; nonzero = key block kept.
- *   row_ptr  int32 [nqb + 1]; col_idx int32 [nnz], ascending within a row. */
+ *   row_ptr  int32 [nqb + 1]; col_idx int32 [nnz], ascending within a row.
+ *
+ * One index may also hold a mask per head or per (batch, head) slice (heads
+ * keep their own statistics: review thread, answer to Q2 of the first review):
+ *   slices      0 or 1: one mask shared by every slice (the layout above);
+ *               H: one per head, shared by the batch elements;
+ *               B*H: one per (batch b, head h), slice b*H + h.
+ *   col_stride  slices > 1: elements from one slice's col_idx to the next's.
+ * Slice s then has its mask at mask + s*nqb*nkb, its row_ptr at
+ * row_ptr + s*(nqb+1) and its col_idx at col_idx + s*col_stride; nnz is the
+ * largest slice's count (nnz <= col_stride).  A zero-initialised tail (slices =
+ * col_stride = 0) is the shared layout. */
 typedef struct {
     int32_t nqb, nkb, nnz;
     const int32_t* row_ptr;
     const int32_t* col_idx;
     const uint8_t* mask;
+    int32_t slices;
+    int32_t col_stride;
 } rettn_index;
 
 /* Build a static block mask on the host.
@@ -110,6 +124,49 @@ rettn_status rettn_index_build(const uint8_t* mask_dev, int32_t nqb, int32_t nkb
                                int32_t* row_ptr_dev, int32_t* col_idx_dev,
                                int32_t* nnz_host, hipStream_t stream);
 
+/* rettn_index_build for `slices` masks at once (one per head or per slice).
+ *   mask_dev    uint8 [slices * nqb * nkb], device.
+ *   row_ptr_dev int32 [slices * (nqb + 1)], device, written.
+ *   col_idx_dev int32 [slices * nqb * nkb], device: slice s's ids start at
+ *               s * nqb * nkb (the index's col_stride is nqb * nkb).
+ *   nnz_host    host int32, written with the largest slice's count.
+ * Synchronises on `stream` once.  RETTN_EINVAL for a null pointer, slices < 1
+ * or sizes beyond 2^31 - 1 elements. */
+rettn_status rettn_index_build_sliced(const uint8_t* mask_dev, int32_t slices, int32_t nqb, int32_t nkb,
+                                      int32_t* row_ptr_dev, int32_t* col_idx_dev, int32_t* nnz_host,
+                                      hipStream_t stream);
+
+/* Dynamic block masks: a mask computed afresh from each step's Q and K, one
+ * per (batch, head) slice.  The pages report applying Re-ttention to such
+ * masks (review thread, answers to W2 and Q1 of the first review: rho stays
+ * predictable, the cached residual no longer matches) but print no rule; the
+ * rule implemented is:
+ *   - every block of query and of key tokens is summarised by its mean (the
+ *     last block by the mean of its tokens < L), in float32;
+ *   - query block a scores key block b by the dot product of the two means;
+ *   - query block a keeps block a itself and the keep - 1 other key blocks with
+ *     the highest scores (all blocks when keep >= nkb); equal scores go to the
+ *     lower block and a score that is not a number ranks below all others.
+ * Every row therefore keeps exactly kk = min(keep, nkb) blocks.
+ *
+ * rettn_dynamic_workspace_bytes: device workspace the call needs for `desc`
+ * (the block means: 2 * B * H * nb * d float32).
+ *
+ * rettn_dynamic_index: writes, for every slice s = b*H + h,
+ *   mask_out    uint8 [B*H * nb * nb], the slice's mask;
+ *   row_ptr_out int32 [B*H * (nb + 1)], row a of slice s at s*(nb+1) + a holds a*kk;
+ *   col_idx_out int32 [B*H * nb * kk], the kept blocks of each row, ascending;
+ * so the matching rettn_index is {nb, nb, nb*kk, row_ptr_out, col_idx_out,
+ * mask_out, slices = B*H, col_stride = nb*kk}.  Q and K follow `desc` (only
+ * B, H, L, d, block, dtype and the strides are used).  Asynchronous: nothing
+ * waits on the host.  RETTN_EINVAL for bad descriptors or pointers, keep < 1,
+ * or a workspace that is null, misaligned (16 bytes) or smaller than the size
+ * above; RETTN_EUNSUPPORTED for more than 2048 blocks per side. */
+rettn_status rettn_dynamic_workspace_bytes(const rettn_desc* desc, size_t* bytes);
+rettn_status rettn_dynamic_index(const rettn_desc* desc, const void* Q, const void* K, int32_t keep,
+                                 void* workspace, size_t workspace_bytes, uint8_t* mask_out,
+                                 int32_t* row_ptr_out, int32_t* col_idx_out, hipStream_t stream);
+
 /* Full-attention calibration step.  For each (b, h) and query row i < L,
  * over every key j < L, with s_j = <q_i, k_j> / sqrt(d) and W(i) the kept keys:
  *   O_i   = softmax(s) V                                  (full attention)
@@ -120,7 +177,7 @@ rettn_status rettn_index_build(const uint8_t* mask_dev, int32_t nqb, int32_t nkb
  * of the first review: both per head and per token).
  * Writes O and R (dtype, descriptor layout) and rho (float32 [B,H,L]).
  * idx must describe a mask of ceil(L/block) x ceil(L/block) blocks (only
- * idx->mask is read).  For bfloat16, the P*V products run with P and V in
+ * idx->mask is read; one per head or slice if idx->slices says so).  For bfloat16, the P*V products run with P and V in
  * float16 (V converted exactly for |V| <= 65504); V beyond that range
  * overflows to infinity in O and R. */
 rettn_status rettn_calibrate(const rettn_desc* desc, const void* Q, const void* K, const void* V,
@@ -154,7 +211,10 @@ rettn_status rettn_calibrate_residual(const rettn_desc* desc, const void* Q, con
  * and third reviews; the ramp-up lambda: answer to W1 of the fourth review;
  * the pages print no ramp formula: this multiplicative, clamped ramp is the
  * reading used).  A row with no kept block gets O'_i = R_i.  Reads rho and R
- * cached by rettn_calibrate; idx->row_ptr and idx->col_idx are walked.
+ * cached by rettn_calibrate; idx->row_ptr and idx->col_idx are walked (those
+ * of the row's own head or slice if idx->slices says so).  The mask need not
+ * be the calibration's: with a dynamic mask the cached rho and R describe
+ * the calibration step's window, as in the pages' trial of dynamic masks.
  * lambda must be finite and >= 0. */
 rettn_status rettn_sparse(const rettn_desc* desc, const void* Q, const void* K, const void* V,
                           const rettn_index* idx, const float* rho, const void* R,

@@ -3,8 +3,10 @@
 The compute path is the HIP library librettn.so (C ABI in include/rettn.h);
 this package is its thin Python binding.
 """
-from .rettn import (BlockIndex, RettnError, calibrate, index_build, lib, mask_build, sparse,
+from .rettn import (BlockIndex, RettnError, calibrate, dynamic_index, dynamic_workspace_bytes, index_build, lib,
+                    mask_build, sparse,
                     MASK_BAND, MASK_COGVIDEO3D, MASK_DIAG, MASK_FULL, RETTN_BF16, RETTN_F32, EXPORTED)
 
-__all__ = ["BlockIndex", "RettnError", "calibrate", "index_build", "lib", "mask_build", "sparse",
+__all__ = ["BlockIndex", "RettnError", "calibrate", "dynamic_index", "dynamic_workspace_bytes", "index_build", "lib",
+           "mask_build", "sparse",
            "MASK_BAND", "MASK_COGVIDEO3D", "MASK_DIAG", "MASK_FULL", "RETTN_BF16", "RETTN_F32", "EXPORTED"]

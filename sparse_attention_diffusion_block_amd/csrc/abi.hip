@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <initializer_list>
+#include <vector>
 
 #include "../../include/rettn.h"
 #include "attn.h"
@@ -30,6 +31,10 @@ rettn_status check_desc(const rettn_desc* d, const rettn_index* idx) {
     if (d->stride_l % gran || d->stride_h % gran || d->stride_b % gran) return RETTN_EINVAL;
     const int64_t nb = cdiv(d->L, d->block);
     if (idx->nqb != nb || idx->nkb != nb) return RETTN_EINVAL;
+    // one shared index, one per head, or one per (batch, head) slice
+    const int64_t S = (int64_t)d->B * d->H;
+    if (idx->slices < 0 || (idx->slices > 1 && idx->slices != d->H && idx->slices != S)) return RETTN_EINVAL;
+    if (idx->slices > 1 && (idx->col_stride < 0 || idx->nnz > idx->col_stride)) return RETTN_EINVAL;
     if ((int64_t)d->B * d->H * nb > 0x7fffffff) return RETTN_EUNSUPPORTED;
     if ((int64_t)d->B * d->H * d->L > ((int64_t)1 << 40)) return RETTN_EUNSUPPORTED;
     return RETTN_OK;
@@ -66,6 +71,9 @@ AttnArgs make_args(const rettn_desc* d, const void* Q, const void* K, const void
     a.d = d->d;
     a.nqb = idx->nqb;
     a.nkb = idx->nkb;
+    // slice of (batch, head) bh: bh % slice_mod (bh < B*H, so B*H gives bh itself)
+    a.slice_mod = idx->slices <= 1 ? 1 : idx->slices == d->H ? d->H : d->B * d->H;
+    a.col_stride = idx->slices <= 1 ? 0 : idx->col_stride;
     a.c = (float)(1.4426950408889634 / sqrt((double)d->d));
     a.ramp = 1.f;
     return a;
@@ -127,16 +135,62 @@ rettn_status rettn_mask_build(const rettn_mask_spec* spec, uint8_t* mask) {
 
 rettn_status rettn_index_build(const uint8_t* mask_dev, int32_t nqb, int32_t nkb, int32_t* row_ptr_dev,
                                int32_t* col_idx_dev, int32_t* nnz_host, hipStream_t stream) {
+    return rettn_index_build_sliced(mask_dev, 1, nqb, nkb, row_ptr_dev, col_idx_dev, nnz_host, stream);
+}
+
+rettn_status rettn_index_build_sliced(const uint8_t* mask_dev, int32_t slices, int32_t nqb, int32_t nkb,
+                                      int32_t* row_ptr_dev, int32_t* col_idx_dev, int32_t* nnz_host,
+                                      hipStream_t stream) {
     if (!mask_dev || !row_ptr_dev || !col_idx_dev || !nnz_host) return RETTN_EINVAL;
     if (nqb < 1 || nkb < 1 || (int64_t)nqb * nkb > 0x7fffffff) return RETTN_EINVAL;
-    if (rettn::launch_index_build(mask_dev, nqb, nkb, row_ptr_dev, col_idx_dev, stream) != hipSuccess)
+    if (slices < 1 || slices > 65535) return RETTN_EINVAL;
+    if (rettn::launch_index_build(mask_dev, slices, nqb, nkb, row_ptr_dev, col_idx_dev, stream) != hipSuccess)
         return RETTN_EHIP;
-    int32_t nnz = 0;
-    if (hipMemcpyAsync(&nnz, row_ptr_dev + nqb, sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    // each slice's total is its last row pointer: gather them (pitch nqb + 1) and take the largest
+    std::vector<int32_t> totals((size_t)slices, 0);
+    if (hipMemcpy2DAsync(totals.data(), sizeof(int32_t), row_ptr_dev + nqb, sizeof(int32_t) * ((size_t)nqb + 1),
+                         sizeof(int32_t), (size_t)slices, hipMemcpyDeviceToHost, stream) != hipSuccess)
         return RETTN_EHIP;
     if (hipStreamSynchronize(stream) != hipSuccess) return RETTN_EHIP;
+    int32_t nnz = 0;
+    for (int32_t t : totals) nnz = t > nnz ? t : nnz;
     *nnz_host = nnz;
     return RETTN_OK;
+}
+
+rettn_status rettn_dynamic_workspace_bytes(const rettn_desc* desc, size_t* bytes) {
+    if (!desc || !bytes) return RETTN_EINVAL;
+    if (desc->B < 1 || desc->H < 1 || desc->L < 1 || desc->d < 1 || desc->d > 128) return RETTN_EINVAL;
+    if (desc->block != 32 && desc->block != 64 && desc->block != 128) return RETTN_EINVAL;
+    *bytes = 2 * sizeof(float) * (size_t)desc->B * (size_t)desc->H * (size_t)cdiv(desc->L, desc->block) *
+             (size_t)desc->d;
+    return RETTN_OK;
+}
+
+rettn_status rettn_dynamic_index(const rettn_desc* desc, const void* Q, const void* K, int32_t keep, void* workspace,
+                                 size_t workspace_bytes, uint8_t* mask_out, int32_t* row_ptr_out,
+                                 int32_t* col_idx_out, hipStream_t stream) {
+    if (!desc) return RETTN_EINVAL;
+    const int64_t nb = cdiv(desc->L > 0 ? desc->L : 1, desc->block > 0 ? desc->block : 1);
+    // the index that the outputs form: its checks are the attention calls' own
+    rettn_index idx{};
+    idx.nqb = idx.nkb = (int32_t)(nb > 0x7fffffff ? 0 : nb);
+    rettn_status st = check_desc(desc, &idx);
+    if (st != RETTN_OK) return st;
+    st = check_tensors({Q, K, workspace});
+    if (st != RETTN_OK) return st;
+    if (!mask_out || check_words({row_ptr_out, col_idx_out}) != RETTN_OK) return RETTN_EINVAL;
+    if (keep < 1) return RETTN_EINVAL;
+    if (nb > 2048 || (int64_t)desc->B * desc->H > 65535) return RETTN_EUNSUPPORTED;
+    size_t need = 0;
+    st = rettn_dynamic_workspace_bytes(desc, &need);
+    if (st != RETTN_OK) return st;
+    if (workspace_bytes < need) return RETTN_EINVAL;
+    const hipError_t e = rettn::launch_dynamic_index(Q, K, desc->dtype == RETTN_BF16, desc->B, desc->H, desc->L,
+                                                     desc->d, desc->block, desc->stride_b, desc->stride_h,
+                                                     desc->stride_l, keep, (float*)workspace, mask_out, row_ptr_out,
+                                                     col_idx_out, stream);
+    return e == hipSuccess ? RETTN_OK : RETTN_EHIP;
 }
 
 rettn_status rettn_calibrate(const rettn_desc* desc, const void* Q, const void* K, const void* V,

@@ -27,6 +27,11 @@ struct AttnArgs {
     int32_t G;                // work-groups in the launch
     int32_t residual;         // calibration's R: 0 masked keys' share of O (Re-ttention), 1 full minus window
                               // attention (the DiTFastAttn comparator)
+    // One index per head or per (batch, head) slice: slice bh % slice_mod (1 = one shared index) has its
+    // mask at mask + slice * nqb * nkb, row_ptr at row_ptr + slice * (nqb + 1), col_idx at
+    // col_idx + slice * col_stride.
+    int32_t slice_mod;
+    int64_t col_stride;
 };
 
 // d is padded to DP in {32, 64, 96, 128} inside the kernels.
@@ -45,7 +50,14 @@ hipError_t launch_sparse64(AttnArgs a, hipStream_t s);
 bool calib_supported(const AttnArgs& a, int block);
 hipError_t launch_calib(AttnArgs a, int block, hipStream_t s);
 
-hipError_t launch_index_build(const uint8_t* mask, int nqb, int nkb, int32_t* row_ptr, int32_t* col_idx,
+// CSR of `slices` masks [slices, nqb, nkb]; slice s's ids start at col_idx + s * nqb * nkb.
+hipError_t launch_index_build(const uint8_t* mask, int slices, int nqb, int nkb, int32_t* row_ptr, int32_t* col_idx,
                               hipStream_t s);
+
+// Dynamic block masks (block means -> scores -> per-row top-kk), one per (batch, head) slice.
+// ws holds 2 * B * H * nb * d floats.
+hipError_t launch_dynamic_index(const void* Q, const void* K, bool bf16, int B, int H, int L, int d, int block,
+                                int64_t sb, int64_t sh, int64_t sl, int keep, float* ws, uint8_t* mask,
+                                int32_t* row_ptr, int32_t* col_idx, hipStream_t s);
 
 }  // namespace rettn

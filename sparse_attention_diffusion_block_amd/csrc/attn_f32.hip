@@ -48,6 +48,9 @@ attn_f32_kernel(const AttnArgs a) {
     const int bh = work / ntile;
     const int tile = work - bh * ntile;
     const int bi = bh / a.H, hi = bh - bi * a.H;
+    const int sl = bh % a.slice_mod;                        // this slice's index
+    const int32_t* rp = a.row_ptr + (int64_t)sl * (a.nqb + 1);
+    const int32_t* ci = a.col_idx + (int64_t)sl * a.col_stride;
     const int64_t base = (int64_t)bi * a.sb + (int64_t)hi * a.sh;
     const int q0 = tile * C::QT + wave * 32;
     const int qb = min(q0 / BLOCK, a.nqb - 1);
@@ -85,10 +88,10 @@ attn_f32_kernel(const AttnArgs a) {
     if constexpr (CALIB) {
         nit = a.nkb;
     } else {
-        e0 = scalar_load(a.row_ptr, qb);
-        nit = scalar_load(a.row_ptr, qb + 1) - e0;
+        e0 = scalar_load(rp, qb);
+        nit = scalar_load(rp, qb + 1) - e0;
     }
-    const int64_t mrow = (int64_t)qb * a.nkb;   // this wave's mask row (calibration)
+    const int64_t mrow = ((int64_t)sl * a.nqb + qb) * a.nkb;   // this wave's mask row (calibration)
 
     f32x16 acc[C::NDT];
     f32x16 acc2[CALIB ? C::NDT : 1];
@@ -134,7 +137,7 @@ attn_f32_kernel(const AttnArgs a) {
     };
     auto kb_of = [&](int it) -> int {
         if constexpr (CALIB) return it;
-        else return scalar_load(a.col_idx, e0 + it);
+        else return scalar_load(ci, e0 + it);
     };
 
     if (nit > 0) {

@@ -73,7 +73,7 @@ __global__ void __launch_bounds__(512) calib_kernel(const AttnArgs a) {
     const int64_t base = (int64_t)bi * a.sb + (int64_t)hi * a.sh;
     const int q0 = tile * C::QT + wave * 32;
     const int qb = min(q0 / BLOCK, a.nqb - 1);     // a wave wholly past L reads the last mask row, stores nothing
-    const int64_t mrow = (int64_t)qb * a.nkb;
+    const int64_t mrow = ((int64_t)(bh % a.slice_mod) * a.nqb + qb) * a.nkb;   // this wave's mask row
     const int row = q0 + n;
     const bool row_ok = row < a.L;
     const uint32_t row_bytes = (uint32_t)a.sl * 2u;

@@ -8,16 +8,21 @@
 //   3. one wave per query block writes its kept block ids in ascending order,
 //      64 at a time: a ballot over the chunk and each lane's rank in it
 //      (mbcnt) give every kept id its slot.
+// Several masks (one per head or per (batch, head) slice) are compacted by
+// the same launches, slice s in grid row s: its mask at s*nqb*nkb, row_ptr at
+// s*(nqb+1), col_idx at s*nqb*nkb.
 // The result is unique, so it is reproduced bit-exactly.
 #include "attn.h"
 #include "common.h"
 
 namespace rettn {
 
-__global__ void __launch_bounds__(64) index_count_kernel(const uint8_t* __restrict__ mask, int nkb,
+__global__ void __launch_bounds__(64) index_count_kernel(const uint8_t* __restrict__ mask, int nqb, int nkb,
                                                          int32_t* __restrict__ row_ptr) {
     const int qb = blockIdx.x;
-    const uint8_t* mrow = mask + (int64_t)qb * nkb;
+    const int64_t sl = blockIdx.y;
+    row_ptr += sl * (nqb + 1);
+    const uint8_t* mrow = mask + (sl * nqb + qb) * nkb;
     int cnt = 0;
     for (int kb = threadIdx.x; kb < nkb; kb += 64) cnt += mrow[kb] != 0;
 #pragma unroll
@@ -29,6 +34,7 @@ __global__ void __launch_bounds__(64) index_count_kernel(const uint8_t* __restri
 }
 
 __global__ void __launch_bounds__(1024) index_scan_kernel(int32_t* __restrict__ row_ptr, int nqb) {
+    row_ptr += (int64_t)blockIdx.x * (nqb + 1);
     __shared__ int32_t part[1024];
     __shared__ int32_t carry;
     const int t = threadIdx.x;
@@ -53,11 +59,14 @@ __global__ void __launch_bounds__(1024) index_scan_kernel(int32_t* __restrict__ 
     }
 }
 
-__global__ void __launch_bounds__(64) index_scatter_kernel(const uint8_t* __restrict__ mask, int nkb,
+__global__ void __launch_bounds__(64) index_scatter_kernel(const uint8_t* __restrict__ mask, int nqb, int nkb,
                                                            const int32_t* __restrict__ row_ptr,
                                                            int32_t* __restrict__ col_idx) {
     const int qb = blockIdx.x;
-    const uint8_t* mrow = mask + (int64_t)qb * nkb;
+    const int64_t sl = blockIdx.y;
+    row_ptr += sl * (nqb + 1);
+    col_idx += sl * nqb * nkb;
+    const uint8_t* mrow = mask + (sl * nqb + qb) * nkb;
     int out = row_ptr[qb];
     for (int kb0 = 0; kb0 < nkb; kb0 += 64) {
         const int kb = kb0 + (int)threadIdx.x;
@@ -69,15 +78,16 @@ __global__ void __launch_bounds__(64) index_scatter_kernel(const uint8_t* __rest
     }
 }
 
-hipError_t launch_index_build(const uint8_t* mask, int nqb, int nkb, int32_t* row_ptr, int32_t* col_idx,
+hipError_t launch_index_build(const uint8_t* mask, int slices, int nqb, int nkb, int32_t* row_ptr, int32_t* col_idx,
                               hipStream_t s) {
-    hipLaunchKernelGGL(index_count_kernel, dim3(nqb), dim3(64), 0, s, mask, nkb, row_ptr);
+    hipLaunchKernelGGL(index_count_kernel, dim3(nqb, slices), dim3(64), 0, s, mask, nqb, nkb, row_ptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(index_scan_kernel, dim3(1), dim3(1024), 0, s, row_ptr, nqb);
+    hipLaunchKernelGGL(index_scan_kernel, dim3(slices), dim3(1024), 0, s, row_ptr, nqb);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(index_scatter_kernel, dim3(nqb), dim3(64), 0, s, mask, nkb, (const int32_t*)row_ptr, col_idx);
+    hipLaunchKernelGGL(index_scatter_kernel, dim3(nqb, slices), dim3(64), 0, s, mask, nqb, nkb,
+                       (const int32_t*)row_ptr, col_idx);
     return hipGetLastError();
 }
 

@@ -82,6 +82,9 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int bh = work / a.nqb;
     const int qb = work - bh * a.nqb;
     const int bi = bh / a.H, hi = bh - bi * a.H;
+    const int sl = bh % a.slice_mod;                        // this slice's CSR
+    const int32_t* rp = a.row_ptr + (int64_t)sl * (a.nqb + 1);
+    const int32_t* ci = a.col_idx + (int64_t)sl * a.col_stride;
     const int64_t base = (int64_t)bi * a.sb + (int64_t)hi * a.sh;
     const int q0 = qb * 64;
     const uint32_t row_bytes = (uint32_t)a.sl * 2u;
@@ -121,8 +124,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         return *(const u32x4*)(slot + r * C::RS + ((c ^ swz(r)) << 3));
     };
 
-    const int e0 = scalar_load(a.row_ptr, qb);
-    const int nit = scalar_load(a.row_ptr, qb + 1) - e0;
+    const int e0 = scalar_load(rp, qb);
+    const int nit = scalar_load(rp, qb + 1) - e0;
 
     // Q tile -> registers: B operand of S^T = K Q^T, Q[q0 + 32 rt + n][16 s + 8 h .. +7]
     // rho of this wave's rows (used in the epilogue; issued first so it is long done by then)
@@ -133,7 +136,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         rho_r[rt] = row < a.L ? a.rho_in[(int64_t)bh * a.L + row] : 0.f;
     }
     // Q tile into the V slot and the first K tile into the K slot, together
-    int kbn = nit > 0 ? scalar_load(a.col_idx, e0) : 0;
+    int kbn = nit > 0 ? scalar_load(ci, e0) : 0;
     load_q(q0);
     if (nit > 0) {
         load_k(kbn * 64);
@@ -236,7 +239,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const int kb = kbn;
         const bool more = it + 1 < nit;
         const bool tail = (kb + 1) * 64 > a.L;
-        kbn = more ? scalar_load(a.col_idx, e0 + it + 1) : 0;
+        kbn = more ? scalar_load(ci, e0 + it + 1) : 0;
 
         wait_vmcnt<0>();                          // K(it) and V(it) have landed
         u32x4 vf[C::NDT][4];

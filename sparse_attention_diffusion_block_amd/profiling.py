@@ -25,6 +25,9 @@ KERNEL_SOURCES = {
     "calib_kernel": ["calib.hip", "common.h", "attn.h"],
     "attn_bf16_kernel": ["attn_bf16.hip", "common.h", "attn.h"],
     "attn_f32_kernel": ["attn_f32.hip", "common.h", "attn.h"],
+    "dyn_pool_kernel": ["dynamic.hip", "common.h", "attn.h"],
+    "dyn_topk_kernel": ["dynamic.hip", "common.h", "attn.h"],
+    "index_": ["index.hip", "common.h", "attn.h"],
 }
 
 

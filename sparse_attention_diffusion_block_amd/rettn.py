@@ -15,8 +15,8 @@ LIB_PATH = os.path.join(_HERE, "librettn.so")
 RETTN_F32, RETTN_BF16 = 0, 1
 MASK_DIAG, MASK_BAND, MASK_COGVIDEO3D, MASK_FULL = 0, 1, 2, 3
 RESIDUAL_MASKED, RESIDUAL_DIFFERENCE = 0, 1
-EXPORTED = ("rettn_mask_build", "rettn_index_build", "rettn_calibrate", "rettn_calibrate_residual", "rettn_sparse",
-            "rettn_status_str")
+EXPORTED = ("rettn_mask_build", "rettn_index_build", "rettn_index_build_sliced", "rettn_dynamic_workspace_bytes",
+            "rettn_dynamic_index", "rettn_calibrate", "rettn_calibrate_residual", "rettn_sparse", "rettn_status_str")
 
 
 class Desc(ctypes.Structure):
@@ -32,7 +32,8 @@ class MaskSpec(ctypes.Structure):
 
 class Index(ctypes.Structure):
     _fields_ = [("nqb", ctypes.c_int32), ("nkb", ctypes.c_int32), ("nnz", ctypes.c_int32),
-                ("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p), ("mask", ctypes.c_void_p)]
+                ("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p), ("mask", ctypes.c_void_p),
+                ("slices", ctypes.c_int32), ("col_stride", ctypes.c_int32)]
 
 
 class RettnError(RuntimeError):
@@ -62,6 +63,12 @@ def lib():
         L.rettn_mask_build.restype = ctypes.c_int
         L.rettn_index_build.argtypes = [vp, i32, i32, vp, vp, ctypes.POINTER(i32), vp]
         L.rettn_index_build.restype = ctypes.c_int
+        L.rettn_index_build_sliced.argtypes = [vp, i32, i32, i32, vp, vp, ctypes.POINTER(i32), vp]
+        L.rettn_index_build_sliced.restype = ctypes.c_int
+        L.rettn_dynamic_workspace_bytes.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_size_t)]
+        L.rettn_dynamic_workspace_bytes.restype = ctypes.c_int
+        L.rettn_dynamic_index.argtypes = [ctypes.POINTER(Desc), vp, vp, i32, vp, ctypes.c_size_t, vp, vp, vp, vp]
+        L.rettn_dynamic_index.restype = ctypes.c_int
         L.rettn_calibrate.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, ctypes.POINTER(Index), vp, vp, vp, vp]
         L.rettn_calibrate.restype = ctypes.c_int
         L.rettn_calibrate_residual.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, ctypes.POINTER(Index), vp, vp, vp,
@@ -88,15 +95,21 @@ def mask_build(kind, nb, w=0, text_blocks=0, tshift=0):
 
 
 class BlockIndex:
-    """A static block mask on the device and its CSR index (kept key blocks per query block)."""
+    """A block mask on the device and its CSR index (kept key blocks per query block).
 
-    def __init__(self, mask, row_ptr, col_idx, nnz, block):
+    `mask` is [nqb, nkb] (one mask for every head) or [S, nqb, nkb] with S = H (one per head) or
+    S = B*H (one per (batch, head) slice, slice b*H + h); row_ptr is [S, nqb + 1] and slice s's
+    column ids start at s * col_stride.  nnz is the largest slice's count."""
+
+    def __init__(self, mask, row_ptr, col_idx, nnz, block, col_stride=0):
         self.mask, self.row_ptr, self.col_idx, self.nnz, self.block = mask, row_ptr, col_idx, nnz, block
-        self.nqb, self.nkb = mask.shape
+        self.nqb, self.nkb = mask.shape[-2:]
+        self.slices = mask.shape[0] if mask.dim() == 3 else 1
+        self.col_stride = col_stride
 
     def c_struct(self):
         return Index(self.nqb, self.nkb, self.nnz, self.row_ptr.data_ptr(), self.col_idx.data_ptr(),
-                     self.mask.data_ptr())
+                     self.mask.data_ptr(), self.slices, self.col_stride)
 
 
 def _stream(device):
@@ -105,17 +118,69 @@ def _stream(device):
 
 
 def index_build(mask, block):
-    """Compact a [nqb, nkb] uint8 mask (host array or device tensor) on the GPU; synchronises once."""
+    """Compact a uint8 mask (host array or device tensor) on the GPU; synchronises once.
+
+    [nqb, nkb]: one mask for every (batch, head); [S, nqb, nkb]: one per head (S = H) or per
+    (batch, head) slice (S = B*H)."""
     import torch
     m = torch.as_tensor(np.asarray(mask) if not isinstance(mask, torch.Tensor) else mask)
     m = m.to(device="cuda", dtype=torch.uint8).contiguous()
-    nqb, nkb = m.shape
-    row_ptr = torch.empty(nqb + 1, dtype=torch.int32, device=m.device)
-    col_idx = torch.empty(max(nqb * nkb, 1), dtype=torch.int32, device=m.device)
     nnz = ctypes.c_int32(0)
-    _check(lib().rettn_index_build(m.data_ptr(), nqb, nkb, row_ptr.data_ptr(), col_idx.data_ptr(),
-                                   ctypes.byref(nnz), _stream(m.device)), "rettn_index_build")
-    return BlockIndex(m, row_ptr, col_idx, nnz.value, block)
+    if m.dim() == 2:
+        nqb, nkb = m.shape
+        row_ptr = torch.empty(nqb + 1, dtype=torch.int32, device=m.device)
+        col_idx = torch.empty(max(nqb * nkb, 1), dtype=torch.int32, device=m.device)
+        _check(lib().rettn_index_build(m.data_ptr(), nqb, nkb, row_ptr.data_ptr(), col_idx.data_ptr(),
+                                       ctypes.byref(nnz), _stream(m.device)), "rettn_index_build")
+        return BlockIndex(m, row_ptr, col_idx, nnz.value, block)
+    if m.dim() != 3:
+        raise ValueError("mask must be [nqb, nkb] or [slices, nqb, nkb]")
+    S, nqb, nkb = m.shape
+    row_ptr = torch.empty((S, nqb + 1), dtype=torch.int32, device=m.device)
+    col_idx = torch.empty(max(S * nqb * nkb, 1), dtype=torch.int32, device=m.device)
+    _check(lib().rettn_index_build_sliced(m.data_ptr(), S, nqb, nkb, row_ptr.data_ptr(), col_idx.data_ptr(),
+                                          ctypes.byref(nnz), _stream(m.device)), "rettn_index_build_sliced")
+    return BlockIndex(m, row_ptr, col_idx, nnz.value, block, col_stride=nqb * nkb)
+
+
+def dynamic_workspace_bytes(q, block):
+    """Device workspace that dynamic_index needs for tensors shaped like q."""
+    n = ctypes.c_size_t(0)
+    desc = _desc(q, block)
+    _check(lib().rettn_dynamic_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)), "rettn_dynamic_workspace_bytes")
+    return n.value
+
+
+def dynamic_index(q, k, keep, block, workspace=None, out=None):
+    """Dynamic block masks of this step's Q and K, one per (batch, head) slice, and their CSR.
+
+    Row a of every slice keeps block a and the keep - 1 other key blocks whose mean key has the
+    largest dot product with the block's mean query.  Asynchronous (no host wait).  `workspace`
+    (uint8 device tensor of at least dynamic_workspace_bytes) and `out` (a BlockIndex from an
+    earlier call of the same shape) may be passed to reuse memory."""
+    import torch
+    q, k = _prep((q, k))
+    B, H, L, d = q.shape
+    if keep < 1:
+        raise ValueError("keep must be at least 1")
+    nb = -(-L // block)
+    kk = min(int(keep), nb)
+    need = dynamic_workspace_bytes(q, block)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        mask = torch.empty((B * H, nb, nb), dtype=torch.uint8, device=q.device)
+        row_ptr = torch.empty((B * H, nb + 1), dtype=torch.int32, device=q.device)
+        col_idx = torch.empty(B * H * nb * kk, dtype=torch.int32, device=q.device)
+        out = BlockIndex(mask, row_ptr, col_idx, nb * kk, block, col_stride=nb * kk)
+    elif out.mask.shape != (B * H, nb, nb) or out.col_stride != nb * kk or out.block != block:
+        raise ValueError("`out` was built for another shape or keep")
+    desc = _desc(q, block)
+    _check(lib().rettn_dynamic_index(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), int(keep), workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(), out.mask.data_ptr(),
+                                     out.row_ptr.data_ptr(), out.col_idx.data_ptr(), _stream(q.device)),
+           "rettn_dynamic_index")
+    return out
 
 
 def _dtype_code(t):

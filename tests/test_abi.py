@@ -143,3 +143,59 @@ def test_calibrate_residual_rejects_unknown_kind(kind):
     for good in (b.RESIDUAL_MASKED, b.RESIDUAL_DIFFERENCE):
         assert lib.rettn_calibrate_residual(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(idx), FAKE, FAKE, FAKE,
                                             good, None) == EINVAL
+
+
+@pytest.mark.parametrize("slices,col_stride,nnz", [(5, 16, 4), (-1, 16, 4), (6, 3, 4), (3, -1, 0)])
+def test_reject_bad_slice_layouts(slices, col_stride, nnz):
+    """An index whose slice count is neither 1, H nor B*H, or whose column stride cannot hold nnz."""
+    lib = rt.lib()
+    d = _good_desc()                     # B = 2, H = 3
+    idx = b.Index(4, 4, nnz, FAKE, FAKE, FAKE, slices, col_stride)
+    assert lib.rettn_calibrate(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(idx), FAKE, FAKE, FAKE, None) == EINVAL
+    assert lib.rettn_sparse(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(idx), FAKE, FAKE, 0.04, 1, FAKE,
+                            None) == EINVAL
+
+
+def test_index_build_sliced_rejects_bad_arguments():
+    lib = rt.lib()
+    nnz = ctypes.c_int32(-1)
+    assert lib.rettn_index_build_sliced(None, 2, 4, 4, FAKE, FAKE, ctypes.byref(nnz), None) == EINVAL
+    assert lib.rettn_index_build_sliced(FAKE, 0, 4, 4, FAKE, FAKE, ctypes.byref(nnz), None) == EINVAL
+    assert lib.rettn_index_build_sliced(FAKE, 70000, 4, 4, FAKE, FAKE, ctypes.byref(nnz), None) == EINVAL
+    assert lib.rettn_index_build_sliced(FAKE, 2, 4, 0, FAKE, FAKE, ctypes.byref(nnz), None) == EINVAL
+    assert nnz.value == -1
+
+
+def test_dynamic_workspace_size():
+    lib = rt.lib()
+    d = _good_desc()                     # B 2, H 3, L 200, d 64, block 64: 4 blocks
+    n = ctypes.c_size_t(0)
+    assert lib.rettn_dynamic_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == 0
+    assert n.value == 2 * 4 * 2 * 3 * 4 * 64
+    assert lib.rettn_dynamic_workspace_bytes(ctypes.byref(d), None) == EINVAL
+    d.block = 48
+    assert lib.rettn_dynamic_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == EINVAL
+
+
+def test_dynamic_index_rejects_bad_arguments():
+    lib = rt.lib()
+    d = _good_desc()
+    need = 2 * 4 * 2 * 3 * 4 * 64
+    ok = dict(q=FAKE, k=FAKE, keep=2, ws=FAKE, ws_bytes=need, mask=FAKE, rp=FAKE, ci=FAKE)
+
+    def call(desc=d, **kw):
+        a = {**ok, **kw}
+        return lib.rettn_dynamic_index(ctypes.byref(desc), a["q"], a["k"], a["keep"], a["ws"], a["ws_bytes"],
+                                       a["mask"], a["rp"], a["ci"], None)
+    assert call(keep=0) == EINVAL
+    assert call(ws_bytes=need - 1) == EINVAL
+    assert call(ws=None) == EINVAL
+    assert call(ws=FAKE + 4) == EINVAL
+    assert call(q=FAKE + 8) == EINVAL
+    assert call(mask=None) == EINVAL
+    assert call(ci=FAKE + 2) == EINVAL
+    bad = _good_desc()
+    bad.d = 60
+    assert call(desc=bad) == EINVAL
+    big = b.Desc(1, 1, 2049 * 32, 64, 32, b.RETTN_BF16, 2049 * 32 * 64, 2049 * 32 * 64, 64)
+    assert call(desc=big, ws_bytes=1 << 40) == 2   # RETTN_EUNSUPPORTED: more than 2048 blocks per side
