@@ -51,6 +51,33 @@ __device__ __forceinline__ float xhalf_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Wave-wide max / min without LDS: DPP swaps partners at distance 1 and 2
+// (quad permutes), then mirrors inside 8 and 16 lanes (each half already
+// reduced, so the mirror meets the other half), then the gfx950 permlane
+// swaps join lanes 16 and 32 apart.  Every lane ends with the result.
+#define RETTN_DPP(X, CTRL) ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)(X), (CTRL), 0xf, 0xf, false))
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, __uint_as_float(RETTN_DPP(__float_as_uint(x), 0xB1)));    // quad_perm [1,0,3,2]
+    x = fmaxf(x, __uint_as_float(RETTN_DPP(__float_as_uint(x), 0x4E)));    // quad_perm [2,3,0,1]
+    x = fmaxf(x, __uint_as_float(RETTN_DPP(__float_as_uint(x), 0x141)));   // row_half_mirror
+    x = fmaxf(x, __uint_as_float(RETTN_DPP(__float_as_uint(x), 0x140)));   // row_mirror
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ int wave_min(int x) {
+    x = min(x, (int)RETTN_DPP(x, 0xB1));
+    x = min(x, (int)RETTN_DPP(x, 0x4E));
+    x = min(x, (int)RETTN_DPP(x, 0x141));
+    x = min(x, (int)RETTN_DPP(x, 0x140));
+    auto r = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+    x = min((int)r[0], (int)r[1]);
+    r = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+    return min((int)r[0], (int)r[1]);
+}
+#undef RETTN_DPP
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Wave-uniform reads of read-only tables (CSR row pointers and column ids,

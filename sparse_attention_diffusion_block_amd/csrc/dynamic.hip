@@ -12,10 +12,11 @@
 //   dyn_pool_kernel  one work-group per (block, slice) reads the block's Q and
 //                    K rows once (16-byte loads) and writes both means (fp32);
 //                    the whole pass is one read of Q and K: HBM-bound.
-//   dyn_topk_kernel  one wave per query block: lane j scores key blocks
+//   dyn_topk_kernel  one wave per R query blocks: lane j scores key blocks
 //                    j, j + 64, ... against the key means staged 64 at a time
-//                    in LDS, then kk - 1 rounds of a wave-wide arg-max pick the
-//                    blocks; the row's mask bytes, CSR row pointer and ascending
+//                    in LDS (each staged tile serves the work-group's 4 R
+//                    query blocks), then per query block kk - 1 rounds of a
+//                    wave-wide arg-max pick the blocks; the row's mask bytes, CSR row pointer and ascending
 //                    column ids are written directly (every row holds exactly
 //                    kk blocks, so no count or scan is needed).
 #include "attn.h"
@@ -83,96 +84,159 @@ __global__ void __launch_bounds__(256) dyn_pool_kernel(const void* __restrict__ 
     }
 }
 
-template <int MM>   // score registers per lane: nb <= 64 * MM
+// MM: score registers per lane (nb <= 64 MM); R: query blocks per wave; DP: d padded to 32/64/96/128
+// (columns d..DP-1 of the staged means are zero, so the dot products run over DP fixed columns)
+template <int MM, int R, int DP>
 __global__ void __launch_bounds__(256) dyn_topk_kernel(const float* __restrict__ qm, const float* __restrict__ km,
                                                        int nb, int d, int kk, uint8_t* __restrict__ mask,
                                                        int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx) {
-    // 64 key means (row stride d + 1: the lanes' reads of one column fall in distinct banks) and the
-    // 4 query means of the work-group
-    __shared__ float kt[64 * 129];
-    __shared__ float qs[4 * 128];
+    // the work-group's 4 R query means (row stride DP), then 64 key means (row stride DP + 1: the
+    // lanes' reads of one column fall in distinct banks)
+    __shared__ __attribute__((aligned(16))) float qs[4 * R * DP];
+    __shared__ float kt[64 * (DP + 1)];
     const int s = blockIdx.y;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int a = blockIdx.x * 4 + wave;   // this wave's query block (>= nb: idle, but joins every barrier)
-    const int ldk = d + 1;
+    const int q0 = blockIdx.x * 4 * R;     // the work-group's first query block
+    const int a0 = q0 + wave * R;          // this wave's first query block
+    constexpr int ldk = DP + 1;
     const float* qms = qm + (int64_t)s * nb * d;
     const float* kms = km + (int64_t)s * nb * d;
-    for (int e = threadIdx.x; e < 4 * d; e += 256) {
-        const int w = e / d, cc = e - w * d;
-        const int ab = blockIdx.x * 4 + w;
-        qs[e] = ab < nb ? qms[(int64_t)ab * d + cc] : 0.f;
+    for (int e = threadIdx.x; e < 4 * R * DP; e += 256) {
+        const int w = e / DP, cc = e % DP;
+        qs[e] = q0 + w < nb && cc < d ? qms[(int64_t)(q0 + w) * d + cc] : 0.f;
     }
-    float sc[MM];
+    // tile staging: thread t copies 16-byte chunk t % cpr of rows t / cpr, t / cpr + rpp, ... (TC
+    // rows cover the tile); the next tile is loaded into registers while the current one is scored
+    constexpr int cpr = DP / 4, rpp = 256 / cpr, TC = (64 + rpp - 1) / rpp;
+    const int c4 = threadIdx.x % cpr, r0 = threadIdx.x / cpr;
+    f32x4 pre[TC];
+    auto load_tile = [&](int m) {
+#pragma unroll
+        for (int i = 0; i < TC; ++i) {
+            const int rr = r0 + i * rpp;
+            const int j = m * 64 + rr;
+            pre[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (r0 < rpp && rr < 64 && j < nb && 4 * c4 < d) pre[i] = *(const f32x4*)(kms + (int64_t)j * d + 4 * c4);
+        }
+    };
+    load_tile(0);
+
+    float sc[R][MM];
 #pragma unroll
     for (int m = 0; m < MM; ++m) {
-        sc[m] = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < R; ++r) sc[r][m] = -INFINITY;
         if (m * 64 < nb) {   // uniform over the work-group
             __syncthreads();
-            for (int e = threadIdx.x; e < 64 * d; e += 256) {
-                const int r = e / d, cc = e - r * d;
-                const int j = m * 64 + r;
-                kt[r * ldk + cc] = j < nb ? kms[(int64_t)j * d + cc] : 0.f;
+#pragma unroll
+            for (int i = 0; i < TC; ++i) {
+                const int rr = r0 + i * rpp;
+                if (r0 < rpp && rr < 64) {
+                    float* dst = kt + rr * ldk + 4 * c4;
+                    dst[0] = pre[i][0];
+                    dst[1] = pre[i][1];
+                    dst[2] = pre[i][2];
+                    dst[3] = pre[i][3];
+                }
             }
             __syncthreads();
+            if ((m + 1) * 64 < nb) load_tile(m + 1);
             const float* kr = kt + lane * ldk;
-            const float* qr = qs + wave * d;
-            float acc = 0.f;
-            for (int cc = 0; cc < d; ++cc) acc = fmaf(qr[cc], kr[cc], acc);
-            sc[m] = acc == acc ? acc : -INFINITY;   // NaN ranks below everything
+            const float* qr = qs + wave * R * DP;
+            float acc[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r] = 0.f;
+#pragma unroll
+            for (int cc = 0; cc < DP; cc += 4) {
+                const float k0 = kr[cc], k1 = kr[cc + 1], k2 = kr[cc + 2], k3 = kr[cc + 3];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const f32x4 qv = *(const f32x4*)(qr + r * DP + cc);
+                    acc[r] = fmaf(qv[0], k0, acc[r]);
+                    acc[r] = fmaf(qv[1], k1, acc[r]);
+                    acc[r] = fmaf(qv[2], k2, acc[r]);
+                    acc[r] = fmaf(qv[3], k3, acc[r]);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) sc[r][m] = acc[r] == acc[r] ? acc[r] : -INFINITY;   // NaN ranks last
         }
     }
-    if (a >= nb) return;
 
-    // bit m of `selb`: block lane + 64 m is kept
-    uint32_t selb = lane == (a & 63) ? 1u << (a >> 6) : 0u;
+    // Selection, the wave's R query blocks in lockstep.  Bit m of selb[r]: block lane + 64 m is kept
+    // by query block a0 + r.  A query block past nb runs along and writes nothing.
+    uint32_t selb[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) selb[r] = a0 + r < nb && lane == ((a0 + r) & 63) ? 1u << ((a0 + r) >> 6) : 0u;
     for (int round = 1; round < kk; ++round) {
-        float bs = -INFINITY;
-        int bj = 0x7fffffff;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float bs = -INFINITY;
+            int bj = 0x7fffffff;
+#pragma unroll
+            for (int m = 0; m < MM; ++m) {
+                const int j = lane + 64 * m;
+                const bool cand = j < nb && ((selb[r] >> m) & 1u) == 0u;
+                if (cand && (sc[r][m] > bs || (sc[r][m] == bs && j < bj))) {
+                    bs = sc[r][m];
+                    bj = j;
+                }
+            }
+            // the best score over the wave, then the lowest block holding it
+            const float top = wave_max(bs);
+            bj = wave_min(bs == top ? bj : 0x7fffffff);
+            if (bj < nb && lane == (bj & 63)) selb[r] |= 1u << (bj >> 6);
+        }
+    }
+
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int a = a0 + r;
+        if (a >= nb) break;
+        const int64_t mrow = ((int64_t)s * nb + a) * nb;
+        int32_t* ci = col_idx + ((int64_t)s * nb + a) * kk;
+        int out = 0;
 #pragma unroll
         for (int m = 0; m < MM; ++m) {
             const int j = lane + 64 * m;
-            const bool cand = j < nb && ((selb >> m) & 1u) == 0u;
-            if (cand && (sc[m] > bs || (sc[m] == bs && j < bj))) {
-                bs = sc[m];
-                bj = j;
-            }
+            const bool keep = j < nb && ((selb[r] >> m) & 1u) != 0u;
+            if (j < nb) mask[mrow + j] = keep ? 1 : 0;
+            const uint64_t bal = __ballot(keep);
+            const int rank =
+                __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+            if (keep) ci[out + rank] = j;
+            out += __popcll(bal);
         }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float os = __shfl_xor(bs, off, 64);
-            const int oj = __shfl_xor(bj, off, 64);
-            if (os > bs || (os == bs && oj < bj)) {
-                bs = os;
-                bj = oj;
-            }
+        if (lane == 0) {
+            int32_t* rp = row_ptr + (int64_t)s * (nb + 1);
+            rp[a] = a * kk;
+            if (a == nb - 1) rp[nb] = nb * kk;
         }
-        if (bj < nb && lane == (bj & 63)) selb |= 1u << (bj >> 6);
-    }
-
-    const int64_t mrow = ((int64_t)s * nb + a) * nb;
-    int32_t* ci = col_idx + ((int64_t)s * nb + a) * kk;
-    int out = 0;
-#pragma unroll
-    for (int m = 0; m < MM; ++m) {
-        const int j = lane + 64 * m;
-        const bool keep = j < nb && ((selb >> m) & 1u) != 0u;
-        if (j < nb) mask[mrow + j] = keep ? 1 : 0;
-        const uint64_t bal = __ballot(keep);
-        const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
-        if (keep) ci[out + rank] = j;
-        out += __popcll(bal);
-    }
-    if (lane == 0) {
-        int32_t* rp = row_ptr + (int64_t)s * (nb + 1);
-        rp[a] = a * kk;
-        if (a == nb - 1) rp[nb] = nb * kk;
     }
 }
 
-template <int MM>
-static void launch_topk(dim3 grid, const float* qm, const float* km, int nb, int d, int kk, uint8_t* mask,
+template <int MM, int R>
+static void launch_topk(int nb, int S, const float* qm, const float* km, int d, int kk, uint8_t* mask,
                         int32_t* row_ptr, int32_t* col_idx, hipStream_t s) {
-    hipLaunchKernelGGL(dyn_topk_kernel<MM>, grid, dim3(256), 0, s, qm, km, nb, d, kk, mask, row_ptr, col_idx);
+    const dim3 grid((nb + 4 * R - 1) / (4 * R), S);
+    switch (pad_d(d)) {
+        case 32:
+            hipLaunchKernelGGL((dyn_topk_kernel<MM, R, 32>), grid, dim3(256), 0, s, qm, km, nb, d, kk, mask, row_ptr,
+                               col_idx);
+            break;
+        case 64:
+            hipLaunchKernelGGL((dyn_topk_kernel<MM, R, 64>), grid, dim3(256), 0, s, qm, km, nb, d, kk, mask, row_ptr,
+                               col_idx);
+            break;
+        case 96:
+            hipLaunchKernelGGL((dyn_topk_kernel<MM, R, 96>), grid, dim3(256), 0, s, qm, km, nb, d, kk, mask, row_ptr,
+                               col_idx);
+            break;
+        default:
+            hipLaunchKernelGGL((dyn_topk_kernel<MM, R, 128>), grid, dim3(256), 0, s, qm, km, nb, d, kk, mask, row_ptr,
+                               col_idx);
+            break;
+    }
 }
 
 hipError_t launch_dynamic_index(const void* Q, const void* K, bool bf16, int B, int H, int L, int d, int block,
@@ -192,14 +256,14 @@ hipError_t launch_dynamic_index(const void* Q, const void* K, bool bf16, int B, 
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 grid((nb + 3) / 4, S);
+    // score registers per lane (MM) and query blocks per wave (R): MM * R <= 32
     const int mm = (nb + 63) / 64;
-    if (mm <= 1) launch_topk<1>(grid, qm, km, nb, d, kk, mask, row_ptr, col_idx, s);
-    else if (mm <= 2) launch_topk<2>(grid, qm, km, nb, d, kk, mask, row_ptr, col_idx, s);
-    else if (mm <= 4) launch_topk<4>(grid, qm, km, nb, d, kk, mask, row_ptr, col_idx, s);
-    else if (mm <= 8) launch_topk<8>(grid, qm, km, nb, d, kk, mask, row_ptr, col_idx, s);
-    else if (mm <= 16) launch_topk<16>(grid, qm, km, nb, d, kk, mask, row_ptr, col_idx, s);
-    else if (mm <= 32) launch_topk<32>(grid, qm, km, nb, d, kk, mask, row_ptr, col_idx, s);
+    if (mm <= 1) launch_topk<1, 4>(nb, S, qm, km, d, kk, mask, row_ptr, col_idx, s);
+    else if (mm <= 2) launch_topk<2, 4>(nb, S, qm, km, d, kk, mask, row_ptr, col_idx, s);
+    else if (mm <= 4) launch_topk<4, 4>(nb, S, qm, km, d, kk, mask, row_ptr, col_idx, s);
+    else if (mm <= 8) launch_topk<8, 4>(nb, S, qm, km, d, kk, mask, row_ptr, col_idx, s);
+    else if (mm <= 16) launch_topk<16, 2>(nb, S, qm, km, d, kk, mask, row_ptr, col_idx, s);
+    else if (mm <= 32) launch_topk<32, 1>(nb, S, qm, km, d, kk, mask, row_ptr, col_idx, s);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

@@ -3,6 +3,7 @@
     python -m sparse_attention_diffusion_block_amd.measure sweep    [--runs 50]
     python -m sparse_attention_diffusion_block_amd.measure configs  [--runs 50]
     python -m sparse_attention_diffusion_block_amd.measure peaks
+    python -m sparse_attention_diffusion_block_amd.measure dynamic  [--runs 50] [--keep 9]
 
 sweep    the sparse step on the shapes of the CogVideoX-2B-like workload (B=2, H=30,
          L=17776, d=64, block 64) under band windows of 75 / 87.5 / 93.8 / 96.9% block
@@ -11,13 +12,19 @@ sweep    the sparse step on the shapes of the CogVideoX-2B-like workload (B=2, H
 configs  calibration and sparse-step times of every workload and mask; the two image
          workloads, whose working sets fit in the 256 MB last-level cache, are also
          timed cold (after writing a 512 MiB buffer before each run).
+dynamic  on the CogVideoX-2B-like shapes: the dynamic block-mask index (block means of Q
+         and K, then a per-row top-keep; one read of Q and K, so HBM-bound), and the sparse
+         step on that per-(batch, head) index beside the static mask shared by all heads
+         and the same static mask given once per head.
 peaks    a measured matrix peak (a large bfloat16 GEMM through the vendor library) and
          a measured copy bandwidth, beside the datasheet figures.
 
-Timing: HIP events on the current stream around one library call, 10 warm-up calls,
-then `--runs` timed calls; median, p10 and p90.  Inputs are the seeded synthetic
-workloads; every call processes all (batch, head) slices.  Output: one JSON object
-per measurement on stdout.
+Timing: HIP events on the current stream around 5 library calls queued back to back
+(behind one more call, so the GPU is busy before the first event and the host's launch
+time stays out of the sample), 10 warm-up calls, then `--runs` samples; median, p10 and
+p90 of the per-call time.  Cold timings flush the cache before every single call.
+Inputs are the seeded synthetic workloads; every call processes all (batch, head)
+slices.  Output: one JSON object per measurement on stdout.
 """
 import argparse
 import json
@@ -34,23 +41,31 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0
 
 
-def _time(fn, runs, warm=10, before=None):
+def _time(fn, runs, warm=10, before=None, reps=5):
+    """Per-call milliseconds: `runs` samples, each `reps` calls back to back between two events
+    (queued behind each other, so the host's own launch time stays out of the sample once the
+    first call is running).  With `before` (a cache flush) every call is its own sample, queued
+    behind the flush, which keeps the GPU busy while it is launched."""
     import torch
     for _ in range(warm):
         if before:
             before()
         fn()
+    reps = 1 if before else reps
     ts = []
     for _ in range(runs):
         if before:
             before()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        if not before:
+            fn()                  # keeps the queue busy while the samples are being launched
         e0.record()
-        fn()
+        for _ in range(reps):
+            fn()
         e1.record()
         e1.synchronize()
-        ts.append(e0.elapsed_time(e1))
+        ts.append(e0.elapsed_time(e1) / reps)
     ts = np.array(ts)
     return {"median_ms": round(float(np.median(ts)), 4), "p10_ms": round(float(np.percentile(ts, 10)), 4),
             "p90_ms": round(float(np.percentile(ts, 90)), 4)}
@@ -141,6 +156,39 @@ def cmd_configs(args):
         torch.cuda.empty_cache()
 
 
+def cmd_dynamic(args):
+    import torch
+    from workloads import CONFIGS
+    from . import rettn as rt
+    cfg = CONFIGS[3]
+    spec = cfg.masks[0]
+    base, drifted, rho, r = _inputs(cfg)
+    q, k, v = drifted
+    nb = -(-cfg.L // cfg.block)
+    ws = torch.empty(rt.dynamic_workspace_bytes(q, cfg.block), dtype=torch.uint8, device="cuda")
+    dyn = rt.dynamic_index(q, k, args.keep, cfg.block, workspace=ws)
+    t = _time(lambda: rt.dynamic_index(q, k, args.keep, cfg.block, workspace=ws, out=dyn), args.runs)
+    nbytes = 2 * cfg.B * cfg.H * cfg.L * cfg.d * 2     # one read of Q and K
+    s_ = t["median_ms"] * 1e-3
+    print(json.dumps({"what": "dynamic_index", "workload": cfg.name, "keep": args.keep, **t,
+                      "algorithmic_gbs": round(nbytes / s_ / 1e9, 1),
+                      "hbm_frac": round(nbytes / s_ / 1e9 / HBM_PEAK_GBS, 4)}), flush=True)
+    static = rt.mask_build(spec.kind, spec.nb, spec.w, spec.text_blocks, spec.tshift)
+    per_head = rt.index_build(np.broadcast_to(static, (cfg.H, nb, nb)).copy(), cfg.block)
+    masks = {"static (shared)": (rt.index_build(static, cfg.block), static[None]),
+             "static (one per head)": (per_head, static[None]),
+             f"dynamic keep {args.keep} (one per slice)": (dyn, dyn.mask.cpu().numpy())}
+    out = torch.empty_like(q)
+    for label, (idx, m) in masks.items():
+        pairs = sum(_counts(cfg, m[i])[3] for i in range(m.shape[0])) / m.shape[0]
+        f_sp = 4.0 * cfg.d * pairs * cfg.B * cfg.H
+        t = _time(lambda: rt.sparse(q, k, v, idx, rho, r, lam=cfg.lam, step=1, out=out), args.runs)
+        s_ = t["median_ms"] * 1e-3
+        print(json.dumps({"what": "sparse_step", "workload": cfg.name, "index": label,
+                          "token_sparsity": round(1.0 - pairs / (cfg.L * cfg.L), 6), **t,
+                          "effective_tflops": round(f_sp / s_ / 1e12, 2)}), flush=True)
+
+
 def cmd_peaks(args):
     import torch
     n = 8192
@@ -163,9 +211,11 @@ def cmd_peaks(args):
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
-    for name in ("sweep", "configs", "peaks"):
+    for name in ("sweep", "configs", "peaks", "dynamic"):
         sp = sub.add_parser(name)
         sp.add_argument("--runs", type=int, default=50)
+        if name == "dynamic":
+            sp.add_argument("--keep", type=int, default=9)
     args = ap.parse_args(argv)
     import torch
     if not torch.cuda.is_available():
@@ -173,7 +223,7 @@ def main(argv=None):
         return 1
     from . import rettn
     rettn.lib()
-    return {"sweep": cmd_sweep, "configs": cmd_configs, "peaks": cmd_peaks}[args.cmd](args) or 0
+    return {"sweep": cmd_sweep, "configs": cmd_configs, "peaks": cmd_peaks, "dynamic": cmd_dynamic}[args.cmd](args) or 0
 
 
 if __name__ == "__main__":

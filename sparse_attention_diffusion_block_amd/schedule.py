@@ -14,11 +14,15 @@ since the refresh.  Nothing of the cache is updated at sparse steps.
     chained_drift_run    a synthetic chain of denoising steps (random-walk drift
                          of Q, K, V) through the schedule, reporting each step's
                          error against true full attention on the same inputs
+    dynamic_mask_run     the same chain with a block mask recomputed from every
+                         step's own Q and K, beside the static mask: how well the
+                         cached rho and R still describe the step's own window
 
 All computation goes through the C ABI (rettn_calibrate / rettn_sparse); this
 module only orders the calls and owns the cache buffers.
 
     python -m sparse_attention_diffusion_block_amd.schedule --config 3 --T 5 --steps 15
+    python -m sparse_attention_diffusion_block_amd.schedule --dynamic --config 3 --T 5 --steps 10
 """
 import argparse
 import json
@@ -156,6 +160,67 @@ def chained_drift_run(config: int = 3, T: int = 5, steps: int = 15, layers: int 
     return records
 
 
+def dynamic_mask_run(config: int = 3, T: int = 5, steps: int = 10, keep: Optional[int] = None,
+                     sigma: Optional[float] = None, lam: Optional[float] = None, log=None) -> List[dict]:
+    """Re-ttention with a dynamic mask beside the workload's static mask, on one drift chain.
+
+    The authors' trial of dynamic masks (review thread, answers to W2 and Q1 of the first
+    review) found the denominator ratio still predictable but the cached residual wrong once the
+    mask moves.  Per step and per mask kind this reports
+      rel_l1_vs_full   the step's output against true full attention;
+      rho_rel_err      the cached, ramped rho against the rho of the step's own window
+                       (sum |rho~ - rho_t| / sum rho_t);
+      r_rel_err        the cached R against the residual of the step's own window;
+      mask_moved       the share of the step's kept blocks that the calibration's mask dropped.
+    `keep` (blocks per row of the dynamic mask) defaults to the static mask's mean row count.
+    At each step a calibration on that step's window gives the true values (it is exact full
+    attention with that window's split); it is a measurement, not part of the method."""
+    import torch
+    from workloads import CONFIGS, drift, make_qkv
+    from . import rettn as rt
+    cfg = CONFIGS[config]
+    spec = cfg.masks[0]
+    sigma = cfg.drift_sigma if sigma is None else sigma
+    lam = cfg.lam if lam is None else lam
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    static_mask = rt.mask_build(spec.kind, spec.nb, spec.w, spec.text_blocks, spec.tshift)
+    static = rt.index_build(static_mask, cfg.block)
+    keep = int(round(static_mask.sum() / static_mask.shape[0])) if keep is None else keep
+    sched = Schedule(T)
+    records = []
+    for kind in ("static", "dynamic"):
+        host = make_qkv(cfg.B, cfg.H, cfg.L, cfg.d, cfg.seed, scale=cfg.input_scale, dtype=cfg.dtype)
+        rho_c = r_c = idx_c = None
+        for t in range(steps):
+            if t > 0:
+                host = drift(*host, cfg.number, t, sigma=sigma, scale=cfg.input_scale, dtype=cfg.dtype)
+            q, k, v = (torch.from_numpy(x).to("cuda").to(dt) for x in host)
+            idx = static if kind == "static" else rt.dynamic_index(q, k, keep, cfg.block)
+            full, rho_t, r_t = rt.calibrate(q, k, v, idx)
+            kstep = sched.k(t)
+            if sched.is_calibration(t):
+                rho_c, r_c, idx_c = rho_t, r_t, idx
+                out = full
+            else:
+                out = rt.sparse(q, k, v, idx, rho_c, r_c, lam=lam, step=kstep)
+            ramped = torch.clamp(rho_c * (1.0 + lam * kstep), max=1.0) if kstep else rho_c
+            m_now, m_cal = idx.mask.bool(), idx_c.mask.bool()
+            moved = float((m_now & ~m_cal).sum()) / max(float(m_now.sum()), 1.0)
+            maxabs, rel = _errors(out, full)
+            rec = {"mask_kind": kind, "step": t, "k": kstep, "T": T, "keep": keep if kind == "dynamic" else None,
+                   "sigma": sigma, "lambda": lam, "workload": cfg.name,
+                   "rel_l1_vs_full": round(rel, 6), "maxabs_vs_full": round(maxabs, 6),
+                   "rho_rel_err": round(float((ramped - rho_t).abs().sum() / rho_t.abs().sum().clamp_min(1e-30)), 6),
+                   "r_rel_err": round(float((r_c.float() - r_t.float()).abs().sum()
+                                            / r_t.float().abs().sum().clamp_min(1e-30)), 6),
+                   "mask_moved": round(moved, 6)}
+            records.append(rec)
+            if log:
+                log(rec)
+    torch.cuda.synchronize()
+    return records
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--config", type=int, default=3)
@@ -164,11 +229,18 @@ def main(argv=None):
     ap.add_argument("--layers", type=int, default=1)
     ap.add_argument("--sigma", type=float, default=None)
     ap.add_argument("--lam", type=float, default=None)
+    ap.add_argument("--dynamic", action="store_true", help="dynamic mask beside the static one")
+    ap.add_argument("--keep", type=int, default=None, help="blocks per row of the dynamic mask")
     args = ap.parse_args(argv)
     import torch
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 1
+    if args.dynamic:
+        for T in args.T:
+            dynamic_mask_run(args.config, T, args.steps, args.keep, args.sigma, args.lam,
+                             log=lambda r: print(json.dumps(r), flush=True))
+        return 0
     for T in args.T:
         chained_drift_run(args.config, T, args.steps, args.layers, args.sigma, args.lam,
                           log=lambda r: print(json.dumps(r), flush=True))

@@ -95,3 +95,27 @@ def test_chain_without_drift_reconstructs_full_attention():
         log(str(rec))
         assert rec["rel_l1_vs_full"] <= 4e-3 and rec["maxabs_vs_full"] <= 2e-2, rec
     assert [r["kind"] for r in recs] == ["calibration", "sparse", "sparse", "sparse", "calibration"]
+
+
+@pytest.mark.gpu
+def test_dynamic_mask_run_invariants():
+    """Calibration steps are exact; the static mask never moves; without drift the dynamic mask
+    stays put and every sparse step rebuilds full attention (lambda = 0) for both mask kinds."""
+    import torch
+    from sparse_attention_diffusion_block_amd.schedule import dynamic_mask_run
+    recs = dynamic_mask_run(config=2, T=3, steps=4, keep=3)
+    torch.cuda.synchronize()
+    for rec in recs:
+        log(str(rec))
+        if rec["k"] == 0:
+            assert rec["rel_l1_vs_full"] == 0.0 and rec["rho_rel_err"] == 0.0 and rec["r_rel_err"] == 0.0
+            assert rec["mask_moved"] == 0.0
+        if rec["mask_kind"] == "static":
+            assert rec["mask_moved"] == 0.0
+    assert {r["mask_kind"] for r in recs} == {"static", "dynamic"}
+    still = dynamic_mask_run(config=2, T=3, steps=3, keep=3, sigma=0.0, lam=0.0)
+    torch.cuda.synchronize()
+    for rec in still:
+        log(str(rec))
+        assert rec["mask_moved"] == 0.0
+        assert rec["rel_l1_vs_full"] <= 4e-3 and rec["maxabs_vs_full"] <= 2e-2, rec
