@@ -186,6 +186,7 @@ def main():
     def mean_ms(pairs_):
         return float(np.mean([a.elapsed_time(b) for a, b in pairs_])) if pairs_ else float("nan")
 
+    sp_each = [a.elapsed_time(b) for a, b in ev["sparse"]]
     t_sp = mean_ms(ev["sparse"]) * 1e-3
     t_cal = mean_ms(ev["calibrate"]) * 1e-3
     t_idx = mean_ms(ev["index"]) * 1e-3
@@ -238,6 +239,9 @@ def main():
                                f"1 calibration + {T} sparse steps per step, lambda={lam}",
                    "global_batch": B, "seq_len": L, "parallelism": "none (1 GPU)"},
         "sparse_step_ms": round(t_sp * 1e3, 4),
+        "sparse_step_ms_p10_p50_p90": [round(float(np.percentile(sp_each, q)), 4) for q in (10, 50, 90)],
+        # mean per launch by steps since the calibration (k = 1 runs right after the calibration)
+        "sparse_step_ms_by_k": [round(float(np.mean(sp_each[j::T])), 4) for j in range(T)],
         "calibrate_ms": round(t_cal * 1e3, 4),
         "index_build_ms": round(t_idx * 1e3, 4),
         "sparse_effective_flops": f_sparse,
