@@ -10,8 +10,10 @@
 // masked tokens' attention, normalised by the full denominator).
 //
 // Design for gfx950 (dense, matrix-core bound):
-//   * a work-group of 8 waves covers 256 query rows (32 per wave) and walks
-//     all key tiles of 64 keys, so each K/V tile fetched from L2 feeds 256 rows;
+//   * a work-group of 4 waves (d <= 64; 8 for d = 96) covers 128 (256) query
+//     rows, 32 per wave, and walks all key tiles of 64 keys, so each K/V tile
+//     fetched from L2 feeds 128 (256) rows; at d <= 64 three work-groups share
+//     a CU, which keeps three waves per SIMD issuing the softmax's vector work;
 //   * K tiles arrive by coalesced direct-to-LDS loads; V tiles by coalesced
 //     16-byte loads that are re-encoded to float16 once per work-group and
 //     written to LDS; both double buffered, one barrier per tile;
@@ -42,7 +44,11 @@ __device__ __forceinline__ float dot2_f16(uint32_t a, float acc) {
 
 template <int DP>
 struct CalCfg {
-    static constexpr int NW = 8;                   // waves per work-group, 32 query rows each
+    // waves per work-group, 32 query rows each.  d <= 64: 4 waves in 168 registers, so three
+    // work-groups share a CU (3 waves per SIMD; the vector work of the softmax issues faster with
+    // more resident waves); d = 96 needs more registers: 8 waves, one work-group per CU.
+    static constexpr int NW = DP <= 64 ? 4 : 8;
+    static constexpr int WPS = DP <= 32 ? 4 : DP <= 64 ? 3 : 2;   // resident waves per SIMD to fit
     static constexpr int NT = NW * 64;
     static constexpr int QT = NW * 32;             // query rows per work-group
     static constexpr int NS = DP / 16;             // k-steps of S^T over d
@@ -55,7 +61,7 @@ struct CalCfg {
 };
 
 template <int BLOCK, int DP>
-__global__ void __launch_bounds__(512) calib_kernel(const AttnArgs a) {
+__global__ void __launch_bounds__(CalCfg<DP>::NT, CalCfg<DP>::WPS) calib_kernel(const AttnArgs a) {
     using C = CalCfg<DP>;
     // [buffer][K | V][64 keys][RS]
     __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * 2 * C::TILE];
