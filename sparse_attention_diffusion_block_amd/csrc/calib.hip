@@ -58,6 +58,10 @@ struct CalCfg {
     static constexpr int TILE = 64 * RS;           // elements per 64-key tile
     static constexpr int KL = TILE / 512 / NW;     // 1 KiB K loads per wave per tile
     static constexpr int VC = TILE / 8 / NT;       // 16-byte V chunks per thread per tile
+    // d = 128: the Q fragments (32 registers) would leave no room for the two accumulator sets at
+    // 2 waves per SIMD, so the group's Q rows sit in LDS (swizzled like K) and are read per tile
+    static constexpr bool QLDS = DP > 96;
+    static constexpr int QSLOT = QLDS ? QT * RS : 8;
 };
 
 template <int BLOCK, int DP>
@@ -65,6 +69,7 @@ __global__ void __launch_bounds__(CalCfg<DP>::NT, CalCfg<DP>::WPS) calib_kernel(
     using C = CalCfg<DP>;
     // [buffer][K | V][64 keys][RS]
     __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * 2 * C::TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t qlds[C::QSLOT];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -95,6 +100,12 @@ __global__ void __launch_bounds__(CalCfg<DP>::NT, CalCfg<DP>::WPS) calib_kernel(
         const int d0 = 16 * s + 8 * h;
         const uint32_t off = d0 < a.d ? (uint32_t)row * row_bytes + 2u * d0 : kOOB;
         qf[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+    }
+    // this wave's rows of the Q slot: row 32 wave + n, logical chunk 2 s + h at chunk (2 s + h) ^ swz(n)
+    uint32_t qoff = (uint32_t)(wave * 32 + n) * C::RS;
+    if constexpr (C::QLDS) {
+#pragma unroll
+        for (int s = 0; s < C::NS; ++s) *(u32x4*)(qlds + qoff + (((2 * s + h) ^ swz(n)) << 3)) = qf[s];
     }
 
     // Tile staging.  K: direct-to-LDS, wave w fills 1 KiB pieces w, w + NW, ...; lane -> (row, physical chunk).
@@ -156,6 +167,7 @@ __global__ void __launch_bounds__(CalCfg<DP>::NT, CalCfg<DP>::WPS) calib_kernel(
         }
         const uint16_t* ks = lds + buf * 2 * C::TILE;
         const uint16_t* vs = ks + C::TILE;
+        if constexpr (C::QLDS) asm volatile("" : "+v"(qoff));   // re-read Q every tile, not kept in registers
 
         // S^T for the tile's two 32-key halves
         f32x16 sacc[2];
@@ -166,8 +178,11 @@ __global__ void __launch_bounds__(CalCfg<DP>::NT, CalCfg<DP>::WPS) calib_kernel(
 #pragma unroll
             for (int s = 0; s < C::NS; ++s) {
                 const u32x4 w = *(const u32x4*)(kr + (((2 * s + h) ^ swn) << 3));
+                u32x4 qv;
+                if constexpr (C::QLDS) qv = *(const u32x4*)(qlds + qoff + (((2 * s + h) ^ swn) << 3));
+                else qv = qf[s];
                 sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w),
-                                                                   __builtin_bit_cast(bf16x8, qf[s]), sacc[kt], 0, 0, 0);
+                                                                   __builtin_bit_cast(bf16x8, qv), sacc[kt], 0, 0, 0);
             }
         }
         if (__builtin_expect((kt64 + 1) * 64 > a.L, 0)) {
@@ -295,17 +310,17 @@ static hipError_t launch(AttnArgs a, hipStream_t s) {
 }
 
 bool calib_supported(const AttnArgs& a, int block) {
-    // d <= 96: two accumulator sets fit beside the fragments without spilling at 2 waves per SIMD
+    // every d up to 128: two accumulator sets fit at 2 waves per SIMD (Q in LDS at d = 128)
     const int64_t slice = ((int64_t)a.L - 1) * a.sl * 2 + (int64_t)a.d * 2;
-    return (block == 64 || block == 128) && a.d <= 96 && slice < ((int64_t)1 << 31);
+    return (block == 64 || block == 128) && a.d <= 128 && slice < ((int64_t)1 << 31);
 }
 
 hipError_t launch_calib(AttnArgs a, int block, hipStream_t s) {
     const int dp = pad_d(a.d);
 #define RETTN_CASE(BL, D) \
     if (block == BL && dp == D) return launch<BL, D>(a, s);
-    RETTN_CASE(64, 32) RETTN_CASE(64, 64) RETTN_CASE(64, 96)
-    RETTN_CASE(128, 32) RETTN_CASE(128, 64) RETTN_CASE(128, 96)
+    RETTN_CASE(64, 32) RETTN_CASE(64, 64) RETTN_CASE(64, 96) RETTN_CASE(64, 128)
+    RETTN_CASE(128, 32) RETTN_CASE(128, 64) RETTN_CASE(128, 96) RETTN_CASE(128, 128)
 #undef RETTN_CASE
     return hipErrorInvalidValue;
 }
