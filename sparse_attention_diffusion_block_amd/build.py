@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librettn.so")
-SOURCES = ["abi.hip", "attn_bf16.hip", "attn_f32.hip", "index.hip", "sparse64.hip", "calib.hip", "dynamic.hip"]
+SOURCES = ["abi.hip", "attn_bf16.hip", "attn_f32.hip", "index.hip", "sparse64.hip", "calib.hip", "dynamic.hip", "sparse_wg.hip"]
 ARCH = "gfx950"
 # Packed fp32 instructions are disabled in all device code.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",

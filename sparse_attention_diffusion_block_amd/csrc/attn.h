@@ -46,7 +46,11 @@ hipError_t launch_sparse_f32(AttnArgs a, int block, hipStream_t s);
 bool sparse64_supported(const AttnArgs& a, int block);
 hipError_t launch_sparse64(AttnArgs a, hipStream_t s);
 
-// Calibration for 64- and 128-token blocks (bfloat16): 256 query rows per work-group.
+// Sparse step for 128-token blocks (bfloat16, d <= 128): one 4-wave work-group per query block.
+bool sparse_wg_supported(const AttnArgs& a, int block);
+hipError_t launch_sparse_wg(AttnArgs a, hipStream_t s);
+
+// Calibration for 64- and 128-token blocks (bfloat16): 128 or 256 query rows per work-group.
 bool calib_supported(const AttnArgs& a, int block);
 hipError_t launch_calib(AttnArgs a, int block, hipStream_t s);
 

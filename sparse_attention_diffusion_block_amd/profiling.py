@@ -25,6 +25,7 @@ KERNEL_SOURCES = {
     "calib_kernel": ["calib.hip", "common.h", "attn.h"],
     "attn_bf16_kernel": ["attn_bf16.hip", "common.h", "attn.h"],
     "attn_f32_kernel": ["attn_f32.hip", "common.h", "attn.h"],
+    "sparse_wg_kernel": ["sparse_wg.hip", "common.h", "attn.h"],
     "dyn_pool_kernel": ["dynamic.hip", "common.h", "attn.h"],
     "dyn_topk_kernel": ["dynamic.hip", "common.h", "attn.h"],
     "index_": ["index.hip", "common.h", "attn.h"],
