@@ -14,7 +14,10 @@
 // registers, so two work-groups share a CU (2 waves per SIMD, 128 KiB of LDS):
 // a SIMD issues the softmax's vector work faster the more waves it holds.  The
 // products, the swizzled LDS tiles, the float16 P*V and the running-reference
-// softmax are those of the calibration kernel.
+// softmax are those of the calibration kernel.  (Instantiated for 128-token
+// blocks only: at 64-token blocks with ~9 kept blocks per query block the
+// per-tile barrier and the per-lane prologue and epilogue cost more than the
+// one-wave-per-query-block sparse64 kernel.)
 #include "attn.h"
 #include "common.h"
 
@@ -32,9 +35,10 @@ __device__ __forceinline__ float dot2_f16(uint32_t a, float acc) {
 
 }  // namespace
 
-template <int DP>
+template <int BLOCK_, int DP>
 struct SwgCfg {
-    static constexpr int BLOCK = 128;
+    static constexpr int BLOCK = BLOCK_;
+    static constexpr int TPB = BLOCK / 64;         // 64-key tiles per key block
     static constexpr int NW = BLOCK / 32;          // waves per work-group, 32 query rows each
     static constexpr int NT = NW * 64;
     static constexpr int NS = DP / 16;             // k-steps of S^T over d
@@ -46,9 +50,9 @@ struct SwgCfg {
     static constexpr int VC = TILE / 8 / NT;       // 16-byte V chunks per thread per tile
 };
 
-template <int DP>
-__global__ void __launch_bounds__(256, 2) sparse_wg_kernel(const AttnArgs a) {
-    using C = SwgCfg<DP>;
+template <int BLOCK, int DP>
+__global__ void __launch_bounds__((SwgCfg<BLOCK, DP>::NT), 2) sparse_wg_kernel(const AttnArgs a) {
+    using C = SwgCfg<BLOCK, DP>;
     // [buffer][K | V][64 keys][RS]
     __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * 2 * C::TILE];
 
@@ -83,10 +87,10 @@ __global__ void __launch_bounds__(256, 2) sparse_wg_kernel(const AttnArgs a) {
     }
     const float rho_c = row_ok ? a.rho_in[(int64_t)bh * a.L + row] : 0.f;
 
-    // 64-key tiles: tile t is half t & 1 of kept block t >> 1 of this query block's CSR row
+    // 64-key tiles: tile t is part t % TPB of kept block t / TPB of this query block's CSR row
     const int e0 = scalar_load(rp, qb);
-    const int ntiles = 2 * (scalar_load(rp, qb + 1) - e0);
-    auto key0 = [&](int t) -> int { return scalar_load(ci, e0 + (t >> 1)) * C::BLOCK + 64 * (t & 1); };
+    const int ntiles = C::TPB * (scalar_load(rp, qb + 1) - e0);
+    auto key0 = [&](int t) -> int { return scalar_load(ci, e0 + t / C::TPB) * C::BLOCK + 64 * (t % C::TPB); };
 
     // Tile staging.  K: direct-to-LDS, wave w fills 1 KiB pieces w, w + NW, ...; lane -> (row, physical chunk).
     // V: thread t holds 16-byte chunks t, t + NT, ... in registers until they are re-encoded and stored.
@@ -259,13 +263,13 @@ __global__ void __launch_bounds__(256, 2) sparse_wg_kernel(const AttnArgs a) {
         }
 }
 
-template <int DP>
+template <int BLOCK, int DP>
 static hipError_t launch(AttnArgs a, hipStream_t s) {
-    using C = SwgCfg<DP>;
+    using C = SwgCfg<BLOCK, DP>;
     const int64_t G = (int64_t)a.B * a.H * a.nqb;
     if (G <= 0 || G > 0x7fffffff) return hipErrorInvalidValue;
     a.G = (int32_t)G;
-    hipLaunchKernelGGL((sparse_wg_kernel<DP>), dim3((unsigned)G), dim3(C::NT), 0, s, a);
+    hipLaunchKernelGGL((sparse_wg_kernel<BLOCK, DP>), dim3((unsigned)G), dim3(C::NT), 0, s, a);
     return hipGetLastError();
 }
 
@@ -277,10 +281,10 @@ bool sparse_wg_supported(const AttnArgs& a, int block) {
 
 hipError_t launch_sparse_wg(AttnArgs a, hipStream_t s) {
     switch (pad_d(a.d)) {
-        case 32: return launch<32>(a, s);
-        case 64: return launch<64>(a, s);
-        case 96: return launch<96>(a, s);
-        default: return launch<128>(a, s);
+        case 32: return launch<128, 32>(a, s);
+        case 64: return launch<128, 64>(a, s);
+        case 96: return launch<128, 96>(a, s);
+        default: return launch<128, 128>(a, s);
     }
 }
 
