@@ -77,6 +77,11 @@ SMALL = [
     ("f32-band-d96-block128", "f32", 2, 1, 190, 96, 128, lambda nb: om.band_mask(nb, 1)),
     ("f32-full-d8", "f32", 1, 1, 100, 8, 32, lambda nb: om.full_mask(nb)),
     ("f32-cog-block32-d128", "f32", 1, 1, 300, 128, 32, lambda nb: om.cogvideo3d_mask(nb, 1, 3)),
+    # 128-token blocks at every padded head dimension (the sparse step's work-group kernel)
+    ("bf16-b128-d32-tail", "bf16", 1, 2, 330, 32, 128, lambda nb: om.band_mask(nb, 2)),
+    ("bf16-b128-d64-emptyrow", "bf16", 2, 1, 520, 64, 128, lambda nb: random_mask(nb, nb, 0.5, 15, empty_rows=(2,))),
+    ("bf16-b128-d96-tail", "bf16", 1, 2, 400, 96, 128, lambda nb: om.cogvideo3d_mask(nb, 1, 2)),
+    ("bf16-b128-d72-full", "bf16", 1, 1, 300, 72, 128, lambda nb: om.full_mask(nb)),
 ]
 
 
