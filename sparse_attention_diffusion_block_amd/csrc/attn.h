@@ -46,9 +46,10 @@ hipError_t launch_sparse_f32(AttnArgs a, int block, hipStream_t s);
 bool sparse64_supported(const AttnArgs& a, int block);
 hipError_t launch_sparse64(AttnArgs a, hipStream_t s);
 
-// Sparse step for 128-token blocks (bfloat16, d <= 128): one 4-wave work-group per query block.
+// Sparse step for 128-token blocks (bfloat16, d <= 128) and 64-token blocks with d > 64: one
+// work-group of block / 32 waves per query block.
 bool sparse_wg_supported(const AttnArgs& a, int block);
-hipError_t launch_sparse_wg(AttnArgs a, hipStream_t s);
+hipError_t launch_sparse_wg(AttnArgs a, int block, hipStream_t s);
 
 // Calibration for 64- and 128-token blocks (bfloat16): 128 or 256 query rows per work-group.
 bool calib_supported(const AttnArgs& a, int block);

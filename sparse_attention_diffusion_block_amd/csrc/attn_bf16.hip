@@ -354,7 +354,7 @@ hipError_t launch_calibrate_bf16(AttnArgs a, int block, hipStream_t s) {
 }
 hipError_t launch_sparse_bf16(AttnArgs a, int block, hipStream_t s) {
     if (sparse64_supported(a, block)) return launch_sparse64(a, s);
-    if (sparse_wg_supported(a, block)) return launch_sparse_wg(a, s);
+    if (sparse_wg_supported(a, block)) return launch_sparse_wg(a, block, s);
     return dispatch<false>(a, block, s);
 }
 

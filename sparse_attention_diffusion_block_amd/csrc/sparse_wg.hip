@@ -1,4 +1,5 @@
-// Sparse step of Re-ttention for bfloat16 with 128-token blocks (any d <= 128).
+// Sparse step of Re-ttention for bfloat16 with 128-token blocks (any d <= 128)
+// and 64-token blocks with 64 < d <= 128.
 //
 // The step (Re-ttention summary page, "Approach"; review thread, replies to
 // W1 of the first and third reviews; ramp-up: answer to W1 of the fourth
@@ -14,10 +15,11 @@
 // registers, so two work-groups share a CU (2 waves per SIMD, 128 KiB of LDS):
 // a SIMD issues the softmax's vector work faster the more waves it holds.  The
 // products, the swizzled LDS tiles, the float16 P*V and the running-reference
-// softmax are those of the calibration kernel.  (Instantiated for 128-token
-// blocks only: at 64-token blocks with ~9 kept blocks per query block the
-// per-tile barrier and the per-lane prologue and epilogue cost more than the
-// one-wave-per-query-block sparse64 kernel.)
+// softmax are those of the calibration kernel.  Also used for 64-token blocks
+// with d > 64 (2-wave groups), where it beats the general kernel; at d <= 64
+// the one-wave-per-query-block sparse64 kernel is faster (with ~9 kept blocks
+// per query block, the per-tile barrier and the per-lane prologue and epilogue
+// weigh more than the extra resident waves).
 #include "attn.h"
 #include "common.h"
 
@@ -276,10 +278,12 @@ static hipError_t launch(AttnArgs a, hipStream_t s) {
 bool sparse_wg_supported(const AttnArgs& a, int block) {
     // buffer offsets are 32-bit: one (batch, head) slice must stay below 2 GiB
     const int64_t slice = ((int64_t)a.L - 1) * a.sl * 2 + (int64_t)a.d * 2;
-    return block == 128 && a.d <= 128 && slice < ((int64_t)1 << 31);
+    // 64-token blocks at d <= 64 belong to sparse64_kernel (faster there)
+    return (block == 128 || (block == 64 && a.d > 64)) && a.d <= 128 && slice < ((int64_t)1 << 31);
 }
 
-hipError_t launch_sparse_wg(AttnArgs a, hipStream_t s) {
+hipError_t launch_sparse_wg(AttnArgs a, int block, hipStream_t s) {
+    if (block == 64) return pad_d(a.d) <= 96 ? launch<64, 96>(a, s) : launch<64, 128>(a, s);
     switch (pad_d(a.d)) {
         case 32: return launch<128, 32>(a, s);
         case 64: return launch<128, 64>(a, s);
