@@ -242,6 +242,11 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         kbn = more ? scalar_load(ci, e0 + it + 1) : 0;
 
         wait_vmcnt<0>();                          // K(it) and V(it) have landed
+        // The next block id comes from a scalar load, and scalar and LDS reads share one counter
+        // that scalar reads may decrement out of order: while it is outstanding the compiler can
+        // only wait for all fragment reads below before the first MFMA.  Consuming it here, behind
+        // the transfer wait, lets each MFMA wait for just the fragments it needs.
+        asm volatile("" ::"s"(kbn));
         u32x4 vf[C::NDT][4];
         {
             u32x4 kf[2][C::NS];                   // A operand: K[64 kb + 32 kt + n][16 s + 8 h .. +7]
