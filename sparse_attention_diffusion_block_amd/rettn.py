@@ -205,6 +205,21 @@ def _prep(tensors):
     return ts
 
 
+def _check_out(t, like, what):
+    """An output tensor the kernels write with `like`'s layout: same device, shape, dtype and strides."""
+    if (not t.is_cuda or t.device != like.device or t.shape != like.shape or t.dtype != like.dtype
+            or t.stride() != like.stride()):
+        raise ValueError(f"{what} must match Q's device, shape, dtype and strides "
+                         f"({tuple(like.shape)}, {like.dtype}, strides {like.stride()})")
+
+
+def _check_rho(rho, q):
+    import torch
+    if (not rho.is_cuda or rho.device != q.device or rho.dtype != torch.float32 or not rho.is_contiguous()
+            or tuple(rho.shape) != tuple(q.shape[:3])):
+        raise ValueError("rho must be a contiguous float32 [B, H, L] tensor on Q's device")
+
+
 def _desc(t, block):
     B, H, L, d = t.shape
     sb, sh, sl, _ = t.stride()
@@ -225,6 +240,9 @@ def calibrate(q, k, v, index, out=None, residual="masked"):
         rho = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
     else:
         o, rho, r = out
+        _check_out(o, q, "out[0] (O)")
+        _check_out(r, q, "out[2] (R)")
+        _check_rho(rho, q)
     desc = _desc(q, index.block)
     idx = index.c_struct()
     kind = {"masked": RESIDUAL_MASKED, "difference": RESIDUAL_DIFFERENCE}[residual]
@@ -238,8 +256,9 @@ def sparse(q, k, v, index, rho, r, lam=0.04, step=1, out=None):
     """Sparse step `step` after a calibration: min(1, rho (1 + lam step)) * window attention + R."""
     import torch
     q, k, v, r = _prep((q, k, v, r))
-    if rho.dtype != torch.float32 or not rho.is_contiguous() or tuple(rho.shape) != tuple(q.shape[:3]):
-        raise ValueError("rho must be a contiguous float32 [B, H, L] tensor")
+    _check_rho(rho, q)
+    if out is not None:
+        _check_out(out, q, "out")
     o = out if out is not None else torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
     desc = _desc(q, index.block)
     idx = index.c_struct()

@@ -260,3 +260,34 @@ def test_sparsity_sweep_c3_shapes(rt):
                                   rows=rows)
         assert_parity(host(o2_g[:, :, rows]), o2_o, cfg.dtype, "sparse O'")
         del o2_g
+
+
+def test_binding_rejects_mismatched_outputs(rt):
+    """Caller-supplied outputs and rho are checked against Q's layout before anything is launched:
+    the kernels write them with Q's strides, so a smaller or differently laid-out tensor would be
+    overrun."""
+    import torch
+    B, H, L, d, block = 1, 2, 256, 64, 64
+    log("case binding output checks")
+    q = dev(bf16_round(np.random.default_rng(5).standard_normal((B, H, L, d)).astype(np.float32)), "bf16")
+    idx = rt.index_build(om.band_mask(L // block, 2), block)
+    o, rho, r = rt.calibrate(q, q, q, idx)
+    bad = [torch.zeros((B, H, L, d), dtype=torch.float32, device=q.device),                 # dtype
+           torch.zeros((B, H, L // 2, d), dtype=torch.bfloat16, device=q.device),          # shape
+           torch.zeros((B, H, d, L), dtype=torch.bfloat16, device=q.device).transpose(2, 3)]  # strides
+    for t in bad:
+        with pytest.raises(ValueError):
+            rt.sparse(q, q, q, idx, rho, r, out=t)
+        with pytest.raises(ValueError):
+            rt.calibrate(q, q, q, idx, out=(t, rho, r))
+        with pytest.raises(ValueError):
+            rt.calibrate(q, q, q, idx, out=(o, rho, t))
+    for bad_rho in (rho.double(), rho[:, :, : L // 2], rho.transpose(0, 1)):
+        with pytest.raises(ValueError):
+            rt.sparse(q, q, q, idx, bad_rho, r)
+        with pytest.raises(ValueError):
+            rt.calibrate(q, q, q, idx, out=(o, bad_rho, r))
+    # matching outputs are accepted and written in place
+    o2 = rt.sparse(q, q, q, idx, rho, r, out=o)
+    torch.cuda.synchronize()
+    assert o2.data_ptr() == o.data_ptr() and torch.isfinite(o2.float()).all()
