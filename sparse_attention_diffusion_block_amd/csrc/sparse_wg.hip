@@ -19,7 +19,11 @@
 // with d > 64 (2-wave groups), where it beats the general kernel; at d <= 64
 // the one-wave-per-query-block sparse64 kernel is faster (with ~9 kept blocks
 // per query block, the per-tile barrier and the per-lane prologue and epilogue
-// weigh more than the extra resident waves).
+// weigh more than the extra resident waves).  At 64-token blocks and d > 64
+// the group keeps a single K and V slot (32 KiB instead of 64) and is compiled
+// for two waves per SIMD, so four groups share a CU: with two or four kept
+// blocks per row there is little to double buffer, and the doubled residency
+// pays more than the exposed K transfer of each later tile.
 #include "attn.h"
 #include "common.h"
 
@@ -50,13 +54,20 @@ struct SwgCfg {
     static constexpr int TILE = 64 * RS;           // elements per 64-key tile
     static constexpr int KL = TILE / 512 / NW;     // 1 KiB K loads per wave per tile
     static constexpr int VC = TILE / 8 / NT;       // 16-byte V chunks per thread per tile
+    // 64-token blocks at d > 64: a 2-wave group with one K and one V slot (32 KiB), so that four
+    // groups share a CU (two waves per SIMD); the next tile's V still comes ahead into registers,
+    // its K after the group has read the current one.  Otherwise both slots are double buffered.
+    static constexpr bool SB = BLOCK == 64 && DP >= 96;
+    static constexpr int NBUF = SB ? 1 : 2;
+    static constexpr int WPE = SB ? 2 : 1;          // resident waves per SIMD to compile for (at least)
 };
 
 template <int BLOCK, int DP>
-__global__ void __launch_bounds__((SwgCfg<BLOCK, DP>::NT), 2) sparse_wg_kernel(const AttnArgs a) {
+__global__ void __launch_bounds__((SwgCfg<BLOCK, DP>::NT), 2) __attribute__((amdgpu_waves_per_eu(SwgCfg<BLOCK, DP>::WPE)))
+sparse_wg_kernel(const AttnArgs a) {
     using C = SwgCfg<BLOCK, DP>;
     // [buffer][K | V][64 keys][RS]
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * 2 * C::TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[C::NBUF * 2 * C::TILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -147,11 +158,11 @@ __global__ void __launch_bounds__((SwgCfg<BLOCK, DP>::NT), 2) sparse_wg_kernel(c
     }
 
     for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
+        const int buf = C::SB ? 0 : t & 1;
         const bool more = t + 1 < ntiles;
         const int knext = more ? key0(t + 1) : 0;
         if (more) {
-            issue_k(knext, buf ^ 1);
+            if constexpr (!C::SB) issue_k(knext, buf ^ 1);
             issue_v(knext);
         }
         const uint16_t* ks = lds + buf * 2 * C::TILE;
@@ -237,9 +248,21 @@ __global__ void __launch_bounds__((SwgCfg<BLOCK, DP>::NT), 2) sparse_wg_kernel(c
             }
         }
 
-        if (more) store_v(buf ^ 1);
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-        __syncthreads();
+        if constexpr (C::SB) {
+            if (more) {
+                // every wave has read this tile's K and V: refill the slots
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                __syncthreads();
+                issue_k(knext, 0);
+                store_v(0);
+                asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+                __syncthreads();
+            }
+        } else {
+            if (more) store_v(buf ^ 1);
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
         kcur = knext;
     }
 

@@ -82,6 +82,10 @@ SMALL = [
     ("bf16-b128-d64-emptyrow", "bf16", 2, 1, 520, 64, 128, lambda nb: random_mask(nb, nb, 0.5, 15, empty_rows=(2,))),
     ("bf16-b128-d96-tail", "bf16", 1, 2, 400, 96, 128, lambda nb: om.cogvideo3d_mask(nb, 1, 2)),
     ("bf16-b128-d72-full", "bf16", 1, 1, 300, 72, 128, lambda nb: om.full_mask(nb)),
+    # 64-token blocks above d = 64 (the single-slot 2-wave groups): an empty row, tails, padded d
+    ("bf16-b64-d96-emptyrow-tail", "bf16", 2, 1, 300, 96, 64,
+     lambda nb: random_mask(nb, nb, 0.5, 16, empty_rows=(1,))),
+    ("bf16-b64-d112-band-tail", "bf16", 1, 2, 460, 112, 64, lambda nb: om.band_mask(nb, 3)),
 ]
 
 
