@@ -9,6 +9,7 @@ rows) run first; then every workload at its full size on sampled rows, in
 the same launch configuration the bench times.
 """
 import math
+import zlib
 
 import numpy as np
 import pytest
@@ -120,7 +121,32 @@ def _run_small(rt, dtype, B, H, L, d, block, make_mask, seed, qk_scale=1.0):
 def test_small_case_all_rows(rt, case):
     name, dtype, B, H, L, d, block, make_mask = case
     log(f"case {name}: dtype={dtype} B={B} H={H} L={L} d={d} block={block}")
-    _run_small(rt, dtype, B, H, L, d, block, make_mask, seed=hash(name) % 1000)
+    _run_small(rt, dtype, B, H, L, d, block, make_mask, seed=zlib.crc32(name.encode()) % 1000)
+
+
+def _random_case(seed):
+    """A seeded draw of dtype, head dimension (any multiple of the 16-byte granule up to 128), block,
+    ragged length, batch / heads, mask density and empty rows."""
+    g = np.random.default_rng(1000 + seed)
+    dtype = "f32" if g.random() < 0.25 else "bf16"
+    gran = 4 if dtype == "f32" else 8
+    d = int(gran * g.integers(1, 128 // gran + 1))
+    block = int(g.choice([32, 64, 128]))
+    L = int(g.integers(1, 640))
+    B, H = int(g.integers(1, 3)), int(g.integers(1, 4))
+    nb = -(-L // block)
+    density = float(g.uniform(0.05, 1.0))
+    empty = tuple(int(x) for x in g.choice(nb, size=min(nb, int(g.integers(0, 3))), replace=False))
+    qk_scale = 2.5 if g.random() < 0.2 else 1.0
+    return dtype, B, H, L, d, block, (lambda n: random_mask(n, n, density, 2000 + seed, empty_rows=empty)), qk_scale
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_shapes_all_rows(rt, seed):
+    """Seeded random shapes through every kernel family the dispatch can pick, on all rows."""
+    dtype, B, H, L, d, block, make_mask, qk_scale = _random_case(seed)
+    log(f"case random-{seed}: dtype={dtype} B={B} H={H} L={L} d={d} block={block} qk_scale={qk_scale}")
+    _run_small(rt, dtype, B, H, L, d, block, make_mask, seed=3000 + seed, qk_scale=qk_scale)
 
 
 @pytest.mark.parametrize("d,block", [(64, 64), (72, 64), (128, 128)])
