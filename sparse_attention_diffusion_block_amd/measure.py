@@ -107,7 +107,17 @@ def _sparse_record(cfg, spec, base, drifted, rho, r, runs, label, before=None):
             "block_sparsity": round(1.0 - float(m.sum()) / m.size, 6),
             "token_sparsity": round(1.0 - pairs / (cfg.L * cfg.L), 6), **t,
             "effective_tflops": round(f_sp / s / 1e12, 2), "mfma_frac": round(f_sp / s / 1e12 / MFMA_PEAK_TFLOPS, 4),
-            "algorithmic_gbs": round(nbytes / s / 1e9, 1), "hbm_frac": round(nbytes / s / 1e9 / HBM_PEAK_GBS, 4)}
+            "algorithmic_gbs": round(nbytes / s / 1e9, 1), "hbm_frac": round(nbytes / s / 1e9 / HBM_PEAK_GBS, 4),
+            **_roofline(f_sp, nbytes, s)}
+
+
+def _roofline(flops, nbytes, s):
+    """Attainable rate at the kernel's arithmetic intensity, min(MFMA peak, AI x HBM peak), and the share
+    of it reached."""
+    ai = flops / nbytes
+    attainable = min(MFMA_PEAK_TFLOPS * 1e12, ai * HBM_PEAK_GBS * 1e9)
+    return {"flop_per_byte": round(ai, 2), "bound": "hbm" if attainable < MFMA_PEAK_TFLOPS * 1e12 else "mfma",
+            "attainable_tflops": round(attainable / 1e12, 1), "roofline_frac": round(flops / s / attainable, 4)}
 
 
 def cmd_sweep(args):
@@ -150,7 +160,8 @@ def cmd_configs(args):
                 s = t["median_ms"] * 1e-3
                 print(json.dumps({"what": "calibrate", "workload": cfg.name, "mask": spec.label(), "timing": label,
                                   **t, "tflops": round(f_cal / s / 1e12, 2),
-                                  "mfma_frac": round(f_cal / s / 1e12 / MFMA_PEAK_TFLOPS, 4)}), flush=True)
+                                  "mfma_frac": round(f_cal / s / 1e12 / MFMA_PEAK_TFLOPS, 4),
+                                  **_roofline(f_cal, nbytes, s)}), flush=True)
                 print(json.dumps(_sparse_record(cfg, spec, base, drifted, rho, r, runs, label, before)), flush=True)
         del base, drifted, rho, r
         torch.cuda.empty_cache()
