@@ -256,15 +256,24 @@ hipError_t launch_dynamic_index(const void* Q, const void* K, bool bf16, int B, 
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // score registers per lane (MM) and query blocks per wave (R): MM * R <= 32
+    // score registers per lane (MM) and query blocks per wave (R): MM * R <= 32, and MM exact up to 8
+    // so that every candidate the selection scans is a real key block
     const int mm = (nb + 63) / 64;
-    if (mm <= 1) launch_topk<1, 4>(nb, S, qm, km, d, kk, mask, row_ptr, col_idx, s);
-    else if (mm <= 2) launch_topk<2, 4>(nb, S, qm, km, d, kk, mask, row_ptr, col_idx, s);
-    else if (mm <= 4) launch_topk<4, 4>(nb, S, qm, km, d, kk, mask, row_ptr, col_idx, s);
-    else if (mm <= 8) launch_topk<8, 4>(nb, S, qm, km, d, kk, mask, row_ptr, col_idx, s);
-    else if (mm <= 16) launch_topk<16, 2>(nb, S, qm, km, d, kk, mask, row_ptr, col_idx, s);
-    else if (mm <= 32) launch_topk<32, 1>(nb, S, qm, km, d, kk, mask, row_ptr, col_idx, s);
-    else return hipErrorInvalidValue;
+    if (mm > 32) return hipErrorInvalidValue;
+    switch (mm) {
+        case 1: launch_topk<1, 4>(nb, S, qm, km, d, kk, mask, row_ptr, col_idx, s); break;
+        case 2: launch_topk<2, 4>(nb, S, qm, km, d, kk, mask, row_ptr, col_idx, s); break;
+        case 3: launch_topk<3, 4>(nb, S, qm, km, d, kk, mask, row_ptr, col_idx, s); break;
+        case 4: launch_topk<4, 4>(nb, S, qm, km, d, kk, mask, row_ptr, col_idx, s); break;
+        case 5: launch_topk<5, 4>(nb, S, qm, km, d, kk, mask, row_ptr, col_idx, s); break;
+        case 6: launch_topk<6, 4>(nb, S, qm, km, d, kk, mask, row_ptr, col_idx, s); break;
+        case 7: launch_topk<7, 4>(nb, S, qm, km, d, kk, mask, row_ptr, col_idx, s); break;
+        case 8: launch_topk<8, 4>(nb, S, qm, km, d, kk, mask, row_ptr, col_idx, s); break;
+        default:
+            if (mm <= 16) launch_topk<16, 2>(nb, S, qm, km, d, kk, mask, row_ptr, col_idx, s);
+            else launch_topk<32, 1>(nb, S, qm, km, d, kk, mask, row_ptr, col_idx, s);
+            break;
+    }
     return hipGetLastError();
 }
 
