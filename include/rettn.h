@@ -178,8 +178,9 @@ rettn_status rettn_dynamic_index(const rettn_desc* desc, const void* Q, const vo
  * Writes O and R (dtype, descriptor layout) and rho (float32 [B,H,L]).
  * idx must describe a mask of ceil(L/block) x ceil(L/block) blocks (only
  * idx->mask is read; one per head or slice if idx->slices says so).  For bfloat16, the P*V products run with P and V in
- * float16 (V converted exactly for |V| <= 65504); V beyond that range
- * overflows to infinity in O and R. */
+ * float16: V converts exactly for 2^-14 <= |V| <= 65504 (and zero), values
+ * below 2^-14 round to float16's subnormal grid (steps of 2^-24), and values
+ * beyond 65504 overflow to infinity in O and R. */
 rettn_status rettn_calibrate(const rettn_desc* desc, const void* Q, const void* K, const void* V,
                              const rettn_index* idx, void* O, float* rho, void* R,
                              hipStream_t stream);
@@ -215,7 +216,8 @@ rettn_status rettn_calibrate_residual(const rettn_desc* desc, const void* Q, con
  * of the row's own head or slice if idx->slices says so).  The mask need not
  * be the calibration's: with a dynamic mask the cached rho and R describe
  * the calibration step's window, as in the pages' trial of dynamic masks.
- * lambda must be finite and >= 0. */
+ * lambda must be finite and >= 0.  For bfloat16, P*V runs in float16 with
+ * V converted as in rettn_calibrate. */
 rettn_status rettn_sparse(const rettn_desc* desc, const void* Q, const void* K, const void* V,
                           const rettn_index* idx, const float* rho, const void* R,
                           float lambda, int32_t step, void* O, hipStream_t stream);
