@@ -321,3 +321,44 @@ def test_binding_rejects_mismatched_outputs(rt):
     o2 = rt.sparse(q, q, q, idx, rho, r, out=o)
     torch.cuda.synchronize()
     assert o2.data_ptr() == o.data_ptr() and torch.isfinite(o2.float()).all()
+
+
+@pytest.mark.timeout(600)
+def test_slice_beyond_32bit_offsets(rt):
+    """One (batch, head) slice larger than 2 GiB (a padded row stride of 16384 elements): the fast
+    kernels address a slice with 32-bit buffer offsets, so such a call must take the general
+    kernels, which use 64-bit addresses.  Calibration and a sparse step on sampled rows, the last
+    row included."""
+    import torch
+    B, H, L, d, block, sl = 1, 1, 65600, 64, 64, 16384
+    assert (L - 1) * sl * 2 + d * 2 >= 1 << 31
+    log(f"case slice over 2 GiB: L={L} d={d} row stride {sl} elements")
+    q, k, v = make_qkv(B, H, L, d, 41, dtype="bf16")
+    q2, k2, v2 = drift(q, k, v, 41, 1, dtype="bf16")
+    nb = -(-L // block)
+    mask = om.band_mask(nb, 3)
+    idx = rt.index_build(mask, block)
+    rows = np.array([0, 1, 63, 64, 32767, 32768, 65535, 65536, L - 1])
+
+    def strided(x):
+        buf = torch.zeros((B, H, L, sl), dtype=torch.bfloat16, device="cuda")
+        view = buf[..., :d]
+        view.copy_(torch.from_numpy(x).to("cuda").to(torch.bfloat16))
+        return view
+
+    tq, tk, tv = (strided(x) for x in (q, k, v))
+    assert tq.stride() == (H * L * sl, L * sl, sl, 1)
+    o_g, rho_g, r_g = rt.calibrate(tq, tk, tv, idx)
+    torch.cuda.synchronize()
+    o_o, rho_o, r_o = oracle.calibrate(q, k, v, mask, block, rows=rows)
+    assert_parity(host(o_g[:, :, rows]), o_o, "bf16", "calibrate O")
+    assert_parity(host(rho_g[:, :, rows]), rho_o, "bf16", "calibrate rho")
+    assert_parity(host(r_g[:, :, rows]), r_o, "bf16", "calibrate R")
+    del tq, tk, tv
+    # the sparse step reads the GPU's own cache on the same strided layout
+    tq2, tk2, tv2 = (strided(x) for x in (q2, k2, v2))
+    o2_g = rt.sparse(tq2, tk2, tv2, idx, rho_g, r_g, lam=0.04, step=1)
+    torch.cuda.synchronize()
+    rho_h, r_h = host(rho_g).astype(np.float64), host(r_g).astype(np.float64)
+    o2_o = oracle.sparse_step(q2, k2, v2, mask, block, rho_h[:, :, rows], r_h[:, :, rows], 0.04, 1, rows=rows)
+    assert_parity(host(o2_g[:, :, rows]), o2_o, "bf16", "sparse O'")
