@@ -189,6 +189,12 @@ DYN = [
     ("bf16-keep1", "bf16", 1, 1, 640, 64, 64, 1),
     ("bf16-keep-all", "bf16", 1, 1, 700, 64, 64, 50),
     ("bf16-one-block", "bf16", 1, 1, 40, 64, 64, 3),
+    # every width of the per-lane score registers: 3, 7, 16 (more than 512 blocks) and 32 (the
+    # largest supported count, 2048 blocks)
+    ("bf16-b64-nb150-tail", "bf16", 1, 1, 150 * 64 - 17, 64, 64, 9),
+    ("bf16-b32-d32-nb420", "bf16", 1, 1, 420 * 32, 32, 32, 9),
+    ("bf16-b64-nb600", "bf16", 1, 1, 600 * 64, 64, 64, 9),
+    ("bf16-b64-nb2048-max", "bf16", 1, 1, 2048 * 64, 64, 64, 9),
 ]
 
 
