@@ -362,3 +362,56 @@ def test_slice_beyond_32bit_offsets(rt):
     rho_h, r_h = host(rho_g).astype(np.float64), host(r_g).astype(np.float64)
     o2_o = oracle.sparse_step(q2, k2, v2, mask, block, rho_h[:, :, rows], r_h[:, :, rows], 0.04, 1, rows=rows)
     assert_parity(host(o2_g[:, :, rows]), o2_o, "bf16", "sparse O'")
+
+
+def test_refresh_period_replays_from_a_hip_graph(rt):
+    """One refresh period (a calibration and four sparse steps, outputs supplied by the caller)
+    captured in a HIP graph: each entry point only launches kernels on the current stream, so the
+    period replays without the host.  Three replays, with the outputs cleared eagerly in between,
+    must each reproduce the eager run bit for bit (the kernels are deterministic)."""
+    import torch
+    B, H, L, d, block = 2, 4, 1000, 64, 64
+    log("case HIP graph of one refresh period")
+    nb = -(-L // block)
+    idx = rt.index_build(om.cogvideo3d_mask(nb, 2, 4), block)
+    sets = [make_qkv(B, H, L, d, 61, dtype="bf16")]
+    for kstep in range(1, 5):
+        sets.append(drift(*sets[-1], 61, kstep, dtype="bf16"))
+    dsets = [tuple(dev(x, "bf16") for x in s) for s in sets]
+    o_cal, r_cal = torch.empty_like(dsets[0][0]), torch.empty_like(dsets[0][0])
+    rho = torch.empty((B, H, L), dtype=torch.float32, device="cuda")
+    o_sp = [torch.empty_like(dsets[0][0]) for _ in range(4)]
+
+    def period():
+        rt.calibrate(*dsets[0], idx, out=(o_cal, rho, r_cal))
+        for kstep in range(1, 5):
+            rt.sparse(*dsets[kstep], idx, rho, r_cal, lam=0.04, step=kstep, out=o_sp[kstep - 1])
+
+    period()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (o_cal, rho, r_cal, *o_sp)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        period()   # warm-up on the capture stream, as torch recommends
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        period()
+    for replay in range(3):
+        for t in (o_cal, rho, r_cal, *o_sp):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, got, ref in zip(("O", "rho", "R", "O'1", "O'2", "O'3", "O'4"), (o_cal, rho, r_cal, *o_sp), want):
+            assert torch.equal(got, ref), f"replay {replay}: {name} differs from the eager run"
+    # and the eager result itself against the oracle on the last sparse step
+    mask = om.cogvideo3d_mask(nb, 2, 4)
+    _, rho_o, r_o = oracle.calibrate(*sets[0], mask, block)
+    rho_in = host(rho)
+    r_in = host(r_cal)
+    o4 = oracle.sparse_step(*sets[4], mask, block, rho_in, r_in, 0.04, 4)
+    assert_parity(host(o_sp[3]), o4, "bf16", "sparse O' (step 4)")
+    assert_parity(rho_in, rho_o, "bf16", "calibrate rho")
