@@ -4,6 +4,7 @@
     python -m sparse_attention_diffusion_block_amd.measure configs  [--runs 50]
     python -m sparse_attention_diffusion_block_amd.measure peaks
     python -m sparse_attention_diffusion_block_amd.measure dynamic  [--runs 50] [--keep 9]
+    python -m sparse_attention_diffusion_block_amd.measure graph    [--runs 50]
 
 sweep    the sparse step on the shapes of the CogVideoX-2B-like workload (B=2, H=30,
          L=17776, d=64, block 64) under band windows of 75 / 87.5 / 93.8 / 96.9% block
@@ -16,6 +17,9 @@ dynamic  on the CogVideoX-2B-like shapes: the dynamic block-mask index (block me
          and K, then a per-row top-keep; one read of Q and K, so HBM-bound), and the sparse
          step on that per-(batch, head) index beside the static mask shared by all heads
          and the same static mask given once per head.
+graph    wall time of one refresh period (a calibration and the sparse steps until the next
+         one, outputs preallocated) on the image and video workloads, launched eagerly from
+         Python and replayed from a HIP graph: what the host's launch path costs per period.
 peaks    a measured matrix peak (a large bfloat16 GEMM through the vendor library) and
          a measured copy bandwidth, beside the datasheet figures.
 
@@ -200,6 +204,60 @@ def cmd_dynamic(args):
                           "effective_tflops": round(f_sp / s_ / 1e12, 2)}), flush=True)
 
 
+def cmd_graph(args):
+    import time
+    import torch
+    from workloads import CONFIGS, drift, make_qkv
+    from . import rettn as rt
+    for n in (2, 3, 4):
+        cfg = CONFIGS[n]
+        spec = cfg.masks[0]
+        T = cfg.sparse_steps
+        dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        sets = [make_qkv(cfg.B, cfg.H, cfg.L, cfg.d, cfg.seed, scale=cfg.input_scale, dtype=cfg.dtype)]
+        for kstep in range(1, T + 1):
+            sets.append(drift(*sets[-1], cfg.number, kstep, sigma=cfg.drift_sigma, scale=cfg.input_scale,
+                              dtype=cfg.dtype))
+        dev = [tuple(torch.from_numpy(x).to("cuda").to(dt) for x in st) for st in sets]
+        del sets
+        idx = rt.index_build(rt.mask_build(spec.kind, spec.nb, spec.w, spec.text_blocks, spec.tshift), cfg.block)
+        o_cal, r_cal = torch.empty_like(dev[0][0]), torch.empty_like(dev[0][0])
+        rho = torch.empty(dev[0][0].shape[:3], dtype=torch.float32, device="cuda")
+        o_sp = [torch.empty_like(dev[0][0]) for _ in range(T)]
+
+        def period():
+            rt.calibrate(*dev[0], idx, out=(o_cal, rho, r_cal))
+            for kstep in range(1, T + 1):
+                rt.sparse(*dev[kstep], idx, rho, r_cal, lam=cfg.lam, step=kstep, out=o_sp[kstep - 1])
+
+        def wall(fn):
+            for _ in range(10):
+                fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.runs):
+                fn()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t0) * 1e3 / args.runs
+
+        eager = wall(period)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            period()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            period()
+        replay = wall(g.replay)
+        print(json.dumps({"what": "refresh_period", "workload": cfg.name, "mask": spec.label(),
+                          "calls": 1 + T, "eager_ms": round(eager, 4), "graph_ms": round(replay, 4),
+                          "graph_speedup": round(eager / replay, 3)}), flush=True)
+        del dev, o_cal, r_cal, rho, o_sp, g
+        torch.cuda.empty_cache()
+
+
 def cmd_peaks(args):
     import torch
     n = 8192
@@ -222,7 +280,7 @@ def cmd_peaks(args):
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
-    for name in ("sweep", "configs", "peaks", "dynamic"):
+    for name in ("sweep", "configs", "peaks", "dynamic", "graph"):
         sp = sub.add_parser(name)
         sp.add_argument("--runs", type=int, default=50)
         if name == "dynamic":
@@ -234,7 +292,8 @@ def main(argv=None):
         return 1
     from . import rettn
     rettn.lib()
-    return {"sweep": cmd_sweep, "configs": cmd_configs, "peaks": cmd_peaks, "dynamic": cmd_dynamic}[args.cmd](args) or 0
+    return {"sweep": cmd_sweep, "configs": cmd_configs, "peaks": cmd_peaks, "dynamic": cmd_dynamic,
+            "graph": cmd_graph}[args.cmd](args) or 0
 
 
 if __name__ == "__main__":
