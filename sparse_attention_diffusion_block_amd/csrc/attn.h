@@ -37,6 +37,17 @@ struct AttnArgs {
 // d is padded to DP in {32, 64, 96, 128} inside the kernels.
 inline int pad_d(int d) { return d <= 32 ? 32 : d <= 64 ? 64 : d <= 96 ? 96 : 128; }
 
+// The fast kernels address one (batch, head) slice through a buffer resource with 32-bit
+// offsets: a row offset (row * stride_l * 2 bytes, rows up to the slice's length rounded up to
+// a whole work tile) plus, for padded 16-byte chunks, an out-of-range offset of 2^31.  A sum
+// that passed 2^32 would wrap onto a valid row, so a slice is taken by these kernels only if
+// every such sum stays below 2^32: rows rounded up to 256, times the row pitch, below
+// 2^31 - 256.  Other slices take the general kernels, which use 64-bit addresses.
+inline bool slice_offsets_fit(const AttnArgs& a) {
+    const int64_t rows = ((int64_t)a.L + 255) / 256 * 256;
+    return rows * a.sl * 2 <= ((int64_t)1 << 31) - 256;
+}
+
 hipError_t launch_calibrate_bf16(AttnArgs a, int block, hipStream_t s);
 hipError_t launch_sparse_bf16(AttnArgs a, int block, hipStream_t s);
 hipError_t launch_calibrate_f32(AttnArgs a, int block, hipStream_t s);

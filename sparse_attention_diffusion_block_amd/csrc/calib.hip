@@ -311,8 +311,7 @@ static hipError_t launch(AttnArgs a, hipStream_t s) {
 
 bool calib_supported(const AttnArgs& a, int block) {
     // every d up to 128: two accumulator sets fit at 2 waves per SIMD (Q in LDS at d = 128)
-    const int64_t slice = ((int64_t)a.L - 1) * a.sl * 2 + (int64_t)a.d * 2;
-    return (block == 64 || block == 128) && a.d <= 128 && slice < ((int64_t)1 << 31);
+    return (block == 64 || block == 128) && a.d <= 128 && slice_offsets_fit(a);
 }
 
 hipError_t launch_calib(AttnArgs a, int block, hipStream_t s) {

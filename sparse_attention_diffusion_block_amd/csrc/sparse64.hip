@@ -375,9 +375,7 @@ static hipError_t launch(AttnArgs a, hipStream_t s) {
 }
 
 bool sparse64_supported(const AttnArgs& a, int block) {
-    // buffer offsets are 32-bit: one (batch, head) slice must stay below 2 GiB
-    const int64_t slice = ((int64_t)a.L - 1) * a.sl * 2 + (int64_t)a.d * 2;
-    return block == 64 && a.d <= 64 && slice < ((int64_t)1 << 31);
+    return block == 64 && a.d <= 64 && slice_offsets_fit(a);
 }
 
 hipError_t launch_sparse64(AttnArgs a, hipStream_t s) {

@@ -299,10 +299,8 @@ static hipError_t launch(AttnArgs a, hipStream_t s) {
 }
 
 bool sparse_wg_supported(const AttnArgs& a, int block) {
-    // buffer offsets are 32-bit: one (batch, head) slice must stay below 2 GiB
-    const int64_t slice = ((int64_t)a.L - 1) * a.sl * 2 + (int64_t)a.d * 2;
     // 64-token blocks at d <= 64 belong to sparse64_kernel (faster there)
-    return (block == 128 || (block == 64 && a.d > 64)) && a.d <= 128 && slice < ((int64_t)1 << 31);
+    return (block == 128 || (block == 64 && a.d > 64)) && a.d <= 128 && slice_offsets_fit(a);
 }
 
 hipError_t launch_sparse_wg(AttnArgs a, int block, hipStream_t s) {

@@ -9,6 +9,8 @@ since the refresh.  Nothing of the cache is updated at sparse steps.
 
     Schedule(T)          which steps calibrate; k = steps since the last refresh
     LayerCache           rho / R / k of one attention layer (device tensors)
+    CacheManager         every layer's cache; state_dict / load_state_dict
+                         checkpoint it to host memory and resume from it
     Rettention           one layer: call it once per denoising step with that
                          step's Q, K, V; it calibrates or runs the sparse step
     chained_drift_run    a synthetic chain of denoising steps (random-walk drift
@@ -80,6 +82,29 @@ class CacheManager:
                 if t is not None:
                     total += t.numel() * t.element_size()
         return total
+
+    def state_dict(self) -> dict:
+        """Host copies of every calibrated layer's cache: the method's only state carried from one
+        denoising step to the next (rho, R and the step of the refresh).  Plain tensors keyed
+        "<layer>.rho", "<layer>.R", "<layer>.refreshed_at", so torch.save / safetensors can store
+        it and a later process can resume the schedule mid-period."""
+        import torch
+        out = {}
+        for layer, c in sorted(self.layers.items()):
+            if c.valid:
+                out[f"{layer}.rho"] = c.rho.detach().cpu().contiguous()
+                out[f"{layer}.R"] = c.R.detach().cpu().contiguous()
+                out[f"{layer}.refreshed_at"] = torch.tensor(c.refreshed_at, dtype=torch.int64)
+        return out
+
+    def load_state_dict(self, state: dict, device="cuda") -> None:
+        """Restore caches saved by state_dict onto `device` (bit for bit)."""
+        layers = sorted({int(key.split(".", 1)[0]) for key in state})
+        for layer in layers:
+            c = self.get(layer)
+            c.rho = state[f"{layer}.rho"].to(device).contiguous()
+            c.R = state[f"{layer}.R"].to(device).contiguous()
+            c.refreshed_at = int(state[f"{layer}.refreshed_at"])
 
 
 class Rettention:

@@ -5,8 +5,10 @@ Each kernel is checked in isolation on identical inputs:
   * calibration: the same (Q, K, V) -> O, rho, R;
   * sparse step: the same (Q', K', V') and the same cached rho / R bits.
 Small cases (all rows, several tiles, ragged tails, padded head dims, empty
-rows) run first; then every workload at its full size on sampled rows, in
-the same launch configuration the bench times.
+rows) run first; then every workload at its full size, in the same launch
+configuration the bench times: the sparse step on every row of every slice
+(the long-video workload on sampled rows), the calibration on sampled rows
+of every slice and on every row of the first and last slice.
 """
 import math
 import zlib
@@ -219,8 +221,13 @@ def test_bitwise_deterministic(rt, d):
                            b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
 
 
-# ------------------------------------------------------------------ full-size workloads, sampled rows
-def _full_config(rt, n, nrows):
+# ------------------------------------------------------------------ full-size workloads
+def _full_config(rt, n, nrows, all_rows):
+    """Workload n at its full size, in the launch configuration the bench times.
+
+    Calibration: sampled rows of every (batch, head) slice, plus (all_rows) every row of the first
+    and the last slice.  Sparse step (steps 1 and T-1 on the seeded synthetic cache): every row of
+    every slice when all_rows, else the sampled rows."""
     import torch
     cfg = CONFIGS[n]
     log(f"config {n} ({cfg.name}): B={cfg.B} H={cfg.H} L={cfg.L} d={cfg.d} block={cfg.block} {cfg.dtype}")
@@ -231,6 +238,7 @@ def _full_config(rt, n, nrows):
     tq, tk, tv = (dev(x, cfg.dtype) for x in (q, k, v))
     tq2, tk2, tv2 = (dev(x, cfg.dtype) for x in (q2, k2, v2))
     trho, tr = torch.from_numpy(rho_c).cuda(), dev(r_c, cfg.dtype)
+    last = (cfg.B - 1, cfg.H - 1)
     for spec in cfg.masks:
         log(f" mask {spec.label()}")
         mask = om.build_mask(spec.kind, spec.nb, spec.w, spec.text_blocks, spec.tshift)
@@ -239,24 +247,37 @@ def _full_config(rt, n, nrows):
         o_g, rho_g, r_g = rt.calibrate(tq, tk, tv, idx)
         torch.cuda.synchronize()
         o_o, rho_o, r_o = oracle.calibrate(q, k, v, mask, cfg.block, rows=rows)
-        assert_parity(host(o_g[:, :, rows]), o_o, cfg.dtype, "calibrate O")
-        assert_parity(host(rho_g[:, :, rows]), rho_o, cfg.dtype, "calibrate rho")
-        assert_parity(host(r_g[:, :, rows]), r_o, cfg.dtype, "calibrate R")
+        assert_parity(host(o_g[:, :, rows]), o_o, cfg.dtype, "calibrate O (sampled rows, all slices)")
+        assert_parity(host(rho_g[:, :, rows]), rho_o, cfg.dtype, "calibrate rho (sampled rows, all slices)")
+        assert_parity(host(r_g[:, :, rows]), r_o, cfg.dtype, "calibrate R (sampled rows, all slices)")
+        if all_rows:
+            for b, h in {(0, 0), last}:
+                sl = (slice(b, b + 1), slice(h, h + 1))
+                o_o, rho_o, r_o = oracle.calibrate(q[sl], k[sl], v[sl], mask, cfg.block)
+                what = f"(all rows of slice b={b} h={h})"
+                assert_parity(host(o_g[sl]), o_o, cfg.dtype, f"calibrate O {what}")
+                assert_parity(host(rho_g[sl]), rho_o, cfg.dtype, f"calibrate rho {what}")
+                assert_parity(host(r_g[sl]), r_o, cfg.dtype, f"calibrate R {what}")
         del o_g, rho_g, r_g
         # sparse step on the synthetic cache, steps 1 and T-1
         for step in sorted({1, cfg.sparse_steps}):
             o2_g = rt.sparse(tq2, tk2, tv2, idx, trho, tr, lam=cfg.lam, step=step)
             torch.cuda.synchronize()
-            o2_o = oracle.sparse_step(q2, k2, v2, mask, cfg.block, rho_c[:, :, rows], r_c[:, :, rows],
-                                      cfg.lam, step, rows=rows)
-            assert_parity(host(o2_g[:, :, rows]), o2_o, cfg.dtype, f"sparse O' step {step}")
+            if all_rows:
+                o2_o = oracle.sparse_step(q2, k2, v2, mask, cfg.block, rho_c, r_c, cfg.lam, step)
+                assert_parity(host(o2_g), o2_o, cfg.dtype, f"sparse O' step {step} (every row of every slice)")
+            else:
+                o2_o = oracle.sparse_step(q2, k2, v2, mask, cfg.block, rho_c[:, :, rows], r_c[:, :, rows],
+                                          cfg.lam, step, rows=rows)
+                assert_parity(host(o2_g[:, :, rows]), o2_o, cfg.dtype, f"sparse O' step {step} (sampled rows)")
             del o2_g
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("n,nrows", [(1, 1024), (2, 96), (3, 48), (4, 96), (5, 12)])
-def test_full_size_config(rt, n, nrows):
-    _full_config(rt, n, nrows)
+@pytest.mark.parametrize("n,nrows,all_rows", [(1, 1024, True), (2, 96, True), (3, 48, True), (4, 96, True),
+                                              (5, 12, False)])
+def test_full_size_config(rt, n, nrows, all_rows):
+    _full_config(rt, n, nrows, all_rows)
 
 
 # ------------------------------------------------------------------ density sweep on the video workload's shapes
@@ -415,3 +436,165 @@ def test_refresh_period_replays_from_a_hip_graph(rt):
     o4 = oracle.sparse_step(*sets[4], mask, block, rho_in, r_in, 0.04, 4)
     assert_parity(host(o_sp[3]), o4, "bf16", "sparse O' (step 4)")
     assert_parity(rho_in, rho_o, "bf16", "calibrate rho")
+
+
+# ------------------------------------------------------------------ reads and stores stay inside the tensor
+GUARD_CASES = [
+    # name, dtype, B, H, L, d, row pitch, block, mask maker
+    ("bf16-b64-d40-tail", "bf16", 1, 3, 300, 40, 56, 64, lambda nb: om.band_mask(nb, 2)),
+    ("bf16-b64-d72-tail", "bf16", 2, 2, 333, 72, 80, 64, lambda nb: om.cogvideo3d_mask(nb, 1, 2)),
+    ("bf16-b128-d48-tail", "bf16", 1, 2, 260, 48, 64, 128, lambda nb: om.band_mask(nb, 2)),
+    ("bf16-b32-d32-tail", "bf16", 1, 2, 130, 32, 40, 32, lambda nb: om.band_mask(nb, 3)),
+    ("f32-b64-d36-tail", "f32", 1, 2, 257, 36, 44, 64, lambda nb: om.band_mask(nb, 2)),
+]
+
+
+@pytest.mark.parametrize("case", GUARD_CASES, ids=[c[0] for c in GUARD_CASES])
+def test_tail_reads_and_stores_stay_inside_the_tensor(rt, case):
+    """Every tensor sits inside a larger buffer: rows past L, 260 guard rows after them and the
+    columns between d and the row pitch hold NaN in the inputs and a sentinel bit pattern in the
+    outputs.  A read outside [0, L) x [0, d) would turn a result into NaN; a store outside it would
+    change a sentinel.  Both steps must give finite results that match the oracle and leave every
+    sentinel (also the one after rho's last element) as it was."""
+    import torch
+    name, dtype, B, H, L, d, pitch, block, make_mask = case
+    log(f"case guard {name}: dtype={dtype} B={B} H={H} L={L} d={d} pitch={pitch} block={block}")
+    G = 260            # more than any kernel's work tile past L, so even an unchecked read stays in the buffer
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    itype = torch.int16 if dtype == "bf16" else torch.int32
+    sentinel = 0x7FC1 if dtype == "bf16" else 0x7FC00001
+
+    def inner(buf):
+        return buf[:, :, :L, :d]
+
+    def guarded_input(x):
+        buf = torch.full((B, H, L + G, pitch), float("nan"), dtype=tdt, device="cuda")
+        inner(buf).copy_(torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to("cuda").to(tdt))
+        return buf
+
+    def guarded_output():
+        return torch.full((B, H, L + G, pitch), sentinel, dtype=itype, device="cuda").view(tdt)
+
+    def outside_unchanged(buf, what):
+        bits = buf.view(itype).clone()
+        inner(bits).fill_(sentinel)
+        assert bool((bits == sentinel).all()), f"{what}: a store landed outside [0, L) x [0, d)"
+
+    scale = 1.0 / math.sqrt(d) if dtype == "f32" else 1.0
+    q, k, v = make_qkv(B, H, L, d, 90, scale=scale, dtype=dtype)
+    nb = -(-L // block)
+    mask = make_mask(nb)
+    idx = rt.index_build(mask, block)
+    bq, bk, bv = (guarded_input(x) for x in (q, k, v))
+    bo, br = guarded_output(), guarded_output()
+    rho_flat = torch.full((B * H * L + 64,), 0x7FC00001, dtype=torch.int32, device="cuda").view(torch.float32)
+    rho = rho_flat[: B * H * L].view(B, H, L)
+    assert inner(bq).stride() == (H * (L + G) * pitch, (L + G) * pitch, pitch, 1)
+    rt.calibrate(inner(bq), inner(bk), inner(bv), idx, out=(inner(bo), rho, inner(br)))
+    torch.cuda.synchronize()
+    outside_unchanged(bo, "calibrate O")
+    outside_unchanged(br, "calibrate R")
+    assert bool((rho_flat[B * H * L:].view(torch.int32) == 0x7FC00001).all()), "calibrate: store past rho's end"
+    o_o, rho_o, r_o = oracle.calibrate(q, k, v, mask, block)
+    assert_parity(host(inner(bo)), o_o, dtype, "calibrate O")
+    assert_parity(host(rho), rho_o, dtype, "calibrate rho")
+    assert_parity(host(inner(br)), r_o, dtype, "calibrate R")
+    # sparse step on drifted inputs, reading the GPU's own cache from the guarded R buffer
+    q2, k2, v2 = drift(q, k, v, 91, 1, scale=scale, dtype=dtype)
+    bq2, bk2, bv2 = (guarded_input(x) for x in (q2, k2, v2))
+    r_in = host(inner(br))
+    rho_in = host(rho)
+    br_in = guarded_input(r_in.astype(np.float32))
+    bo2 = guarded_output()
+    rt.sparse(inner(bq2), inner(bk2), inner(bv2), idx, rho, inner(br_in), lam=0.04, step=2, out=inner(bo2))
+    torch.cuda.synchronize()
+    outside_unchanged(bo2, "sparse O'")
+    o2_o = oracle.sparse_step(q2, k2, v2, mask, block, rho_in, r_in, 0.04, 2)
+    assert_parity(host(inner(bo2)), o2_o, dtype, "sparse O'")
+
+
+# ------------------------------------------------------------------ the float16 P*V domain of V
+FAMILIES = [
+    # name, B, H, L, d, block: one case per kernel family of the bf16 dispatch
+    ("b64-d64", 1, 2, 300, 64, 64),       # calibration work-groups of 4 waves; one wave per query block
+    ("b64-d72", 1, 2, 300, 72, 64),       # d padded to 96: 8-wave calibration groups; 2-wave sparse groups
+    ("b128-d128", 1, 1, 300, 128, 128),   # Q in LDS for the calibration; 4-wave sparse groups
+    ("b32-d64", 1, 2, 200, 64, 32),       # the general kernels
+]
+
+
+@pytest.mark.parametrize("fam", FAMILIES, ids=[f[0] for f in FAMILIES])
+def test_fp16_pv_overflow_gives_infinity(rt, fam):
+    """P*V runs with V re-encoded to float16, whose largest finite value is 65504: a bfloat16 V
+    entry of 2^17 becomes +inf, as the header documents.  Calibration: column d0 of O is +inf in
+    every row (every key has a positive probability), R is +inf exactly where that key is masked
+    and matches the oracle where it is kept; every other column matches the oracle.  Sparse step:
+    O' is +inf in column d0 exactly for rows whose window holds the key."""
+    import torch
+    name, B, H, L, d, block = fam
+    log(f"case fp16 overflow {name}: B={B} H={H} L={L} d={d} block={block}")
+    q, k, v = make_qkv(B, H, L, d, 95)
+    q, k = bf16_round(q * np.float32(0.25)), bf16_round(k * np.float32(0.25))   # no probability underflows
+    j0, d0 = 137, 5
+    v[:, :, j0, d0] = 131072.0                                                  # 2^17: exact in bfloat16
+    nb = -(-L // block)
+    mask = om.band_mask(nb, 2)
+    idx = rt.index_build(mask, block)
+    o_g, rho_g, r_g = rt.calibrate(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), idx)
+    torch.cuda.synchronize()
+    o_g, rho_g, r_g = host(o_g), host(rho_g), host(r_g)
+    o_o, rho_o, r_o = oracle.calibrate(q, k, v, mask, block)
+    kept = mask[np.arange(L) // block, j0 // block] != 0        # rows whose window holds key j0
+    assert np.all(o_g[..., d0] == np.inf)
+    assert np.all(r_g[:, :, ~kept, d0] == np.inf)
+    others = [c for c in range(d) if c != d0]
+    assert_parity(o_g[..., others], o_o[..., others], "bf16", "calibrate O (other columns)")
+    assert_parity(rho_g, rho_o, "bf16", "calibrate rho")
+    assert_parity(r_g[..., others], r_o[..., others], "bf16", "calibrate R (other columns)")
+    assert_parity(r_g[:, :, kept, d0], r_o[:, :, kept, d0], "bf16", "calibrate R (column d0, key kept)")
+    rho_c, r_c = make_cache(B, H, L, d, seed=96)
+    o2 = host(rt.sparse(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), idx, torch.from_numpy(rho_c).cuda(),
+                        dev(r_c, "bf16"), lam=0.04, step=1))
+    o2_o = oracle.sparse_step(q, k, v, mask, block, rho_c, r_c, 0.04, 1)
+    assert np.all(o2[:, :, kept, d0] == np.inf)
+    assert_parity(o2[:, :, ~kept, d0], o2_o[:, :, ~kept, d0], "bf16", "sparse O' (column d0, key masked)")
+    assert_parity(o2[..., others], o2_o[..., others], "bf16", "sparse O' (other columns)")
+
+
+@pytest.mark.parametrize("fam", FAMILIES, ids=[f[0] for f in FAMILIES])
+def test_fp16_pv_subnormal_values_round_to_the_grid(rt, fam):
+    """V entries below 2^-14 fall on float16's subnormal grid (steps of 2^-24).  With V ~ N(0,1) * 2^-16
+    most entries are subnormal in float16; the header documents an absolute error of at most 2^-25
+    per entry, so the outputs may differ from the oracle by that plus the usual float16 P and
+    bfloat16 output rounding: |err| <= 2^-25 + 2^-10 max|V| + 2^-8 |ref|.  Dropping these values
+    (a flush to zero) would miss by about |ref| itself, far above the bound."""
+    import torch
+    name, B, H, L, d, block = fam
+    log(f"case fp16 subnormal {name}: B={B} H={H} L={L} d={d} block={block}")
+    q, k, v = make_qkv(B, H, L, d, 97)
+    v = bf16_round(v * np.float32(2.0 ** -16))
+    assert np.mean(np.abs(v) < 2.0 ** -14) > 0.9
+    nb = -(-L // block)
+    mask = om.band_mask(nb, 2)
+    idx = rt.index_build(mask, block)
+    o_g, rho_g, r_g = rt.calibrate(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), idx)
+    torch.cuda.synchronize()
+    o_o, rho_o, r_o = oracle.calibrate(q, k, v, mask, block)
+    vmax = float(np.abs(v).max())
+
+    def within(g, ref, what):
+        bound = 2.0 ** -25 + 2.0 ** -10 * vmax + 2.0 ** -8 * np.abs(ref)
+        err = np.abs(g - ref)
+        log(f"  {what}: max err {err.max():.3e}, max |ref| {np.abs(ref).max():.3e}, worst err/bound "
+            f"{float((err / bound).max()):.3f}")
+        assert np.all(np.isfinite(g)) and np.all(err <= bound), what
+
+    within(host(o_g), o_o, "calibrate O")
+    within(host(r_g), r_o, "calibrate R")
+    assert_parity(host(rho_g), rho_o, "bf16", "calibrate rho")
+    rho_in = rho_o.astype(np.float32)
+    r_in = bf16_round(r_o.astype(np.float32))
+    o2 = rt.sparse(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), idx, torch.from_numpy(rho_in).cuda(),
+                   dev(r_in, "bf16"), lam=0.04, step=2)
+    torch.cuda.synchronize()
+    within(host(o2), oracle.sparse_step(q, k, v, mask, block, rho_in, r_in, 0.04, 2), "sparse O'")

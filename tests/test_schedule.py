@@ -119,3 +119,62 @@ def test_dynamic_mask_run_invariants():
         log(str(rec))
         assert rec["mask_moved"] == 0.0
         assert rec["rel_l1_vs_full"] <= 4e-3 and rec["maxabs_vs_full"] <= 2e-2, rec
+
+
+def test_cache_state_dict_round_trip_on_cpu(tmp_path):
+    """The checkpoint format: host tensors keyed per layer, saved with torch.save and loaded back
+    with weights_only=True (nothing in the file is executed); only calibrated layers are saved."""
+    import torch
+    cm = CacheManager()
+    c = cm.get(4)
+    c.rho = torch.rand(1, 2, 5)
+    c.R = torch.randn(1, 2, 5, 8).to(torch.bfloat16)
+    c.refreshed_at = 10
+    cm.get(7)                                   # never calibrated: not saved
+    path = tmp_path / "cache.pt"
+    torch.save(cm.state_dict(), path)
+    back = CacheManager()
+    back.load_state_dict(torch.load(path, weights_only=True), device="cpu")
+    assert sorted(back.layers) == [4]
+    d = back.get(4)
+    assert d.refreshed_at == 10 and d.valid
+    assert torch.equal(d.rho.view(torch.int32), c.rho.view(torch.int32))
+    assert torch.equal(d.R.view(torch.int16), c.R.view(torch.int16))
+
+
+@pytest.mark.gpu
+def test_checkpoint_resume_is_bit_identical(tmp_path):
+    """The method's only cross-step state is the cache of rho and R (review thread, answer to Q4 of
+    the first review: the residual cache).  Calibrate at step 0, checkpoint the cache to a file,
+    reload it in a fresh cache manager and resume the schedule at step 3: every sparse step of the
+    resumed run equals the uninterrupted run bit for bit."""
+    import torch
+    import sparse_attention_diffusion_block_amd as rt
+    B, H, L, d, block, seed, T = 2, 3, 700, 64, 64, 21, 5
+    nb = -(-L // block)
+    idx = rt.index_build(rt.mask_build(rt.MASK_COGVIDEO3D, nb, text_blocks=1, tshift=3), block)
+    sets = [make_qkv(B, H, L, d, seed)]
+    for t in range(1, T):
+        sets.append(drift(*sets[-1], seed, t))
+    dsets = [tuple(dev(x, "bf16") for x in s) for s in sets]
+    log("checkpoint: uninterrupted run")
+    live = Rettention(idx, Schedule(T), CacheManager(), layer=2)
+    want = [live(t, *dsets[t]).clone() for t in range(T)]
+    torch.cuda.synchronize()
+    # the same calibration, checkpointed after step 0
+    first = Rettention(idx, Schedule(T), CacheManager(), layer=2)
+    first(0, *dsets[0])
+    torch.cuda.synchronize()
+    path = tmp_path / "rettn_cache.pt"
+    torch.save(first.cache.state_dict(), path)
+    log(f"checkpoint: {path.stat().st_size} bytes written; resuming at step 3")
+    cache = CacheManager()
+    cache.load_state_dict(torch.load(path, weights_only=True), device="cuda")
+    c0, c1 = first.cache.get(2), cache.get(2)
+    assert torch.equal(c0.rho.view(torch.int32), c1.rho.view(torch.int32))
+    assert torch.equal(c0.R.view(torch.int16), c1.R.view(torch.int16))
+    resumed = Rettention(idx, Schedule(T), cache, layer=2)
+    for t in range(3, T):
+        got = resumed(t, *dsets[t])
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), want[t].view(torch.int16)), f"step {t} differs after resuming"
