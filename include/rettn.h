@@ -20,7 +20,9 @@
  *     [B, H, L] device array.  The element type is the descriptor's dtype
  *     (float32 or bfloat16); rho is always float32.
  *   - The caller owns every buffer.  The library allocates no device
- *     memory and keeps no state between calls besides its code objects.
+ *     memory and keeps no state between calls besides its code objects
+ *     (one of which holds the static scratch array of
+ *     rettn_dynamic_index_noalloc, with its device address cached per GPU).
  *   - Launches are asynchronous on the given HIP stream (NULL = the null
  *     stream); results are valid once the stream is ordered after them.
  *   - Errors are returned as status codes; nothing throws or aborts.  All
@@ -43,7 +45,9 @@ typedef enum {
     RETTN_OK = 0,
     RETTN_EINVAL = 1,        /* a bad argument: null pointer, size, stride, alignment, mismatch */
     RETTN_EUNSUPPORTED = 2,  /* a valid request outside what the kernels implement */
-    RETTN_EHIP = 3           /* a HIP runtime call or kernel launch failed */
+    RETTN_EHIP = 3,          /* a HIP runtime call or kernel launch failed */
+    RETTN_ESCRATCH = 4       /* the request needs more than the library's static scratch
+                                (rettn_dynamic_index_noalloc only) */
 } rettn_status;
 
 typedef enum { RETTN_F32 = 0, RETTN_BF16 = 1 } rettn_dtype;
@@ -166,6 +170,25 @@ rettn_status rettn_dynamic_workspace_bytes(const rettn_desc* desc, size_t* bytes
 rettn_status rettn_dynamic_index(const rettn_desc* desc, const void* Q, const void* K, int32_t keep,
                                  void* workspace, size_t workspace_bytes, uint8_t* mask_out,
                                  int32_t* row_ptr_out, int32_t* col_idx_out, hipStream_t stream);
+
+/* rettn_dynamic_index without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops,
+ * harnesses that forbid hipMalloc).  The block means live in a static device
+ * array of RETTN_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held
+ * until the process ends; its device address is looked up once per device on
+ * the first call made with that device current.  The call itself allocates
+ * nothing.  Outputs, validation and results are those of rettn_dynamic_index
+ * (bit for bit).  A request whose block means exceed the array
+ * (rettn_dynamic_workspace_bytes > RETTN_NOALLOC_SCRATCH_BYTES) returns
+ * RETTN_ESCRATCH and launches nothing; a failed symbol lookup returns
+ * RETTN_EHIP.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (on different streams, or from different threads without
+ * ordering) race and must be serialised by the caller.  Nothing in the array
+ * needs to start at zero (every mean is written before it is read). */
+#define RETTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+rettn_status rettn_dynamic_index_noalloc(const rettn_desc* desc, const void* Q, const void* K, int32_t keep,
+                                         uint8_t* mask_out, int32_t* row_ptr_out, int32_t* col_idx_out,
+                                         hipStream_t stream);
 
 /* Full-attention calibration step.  For each (b, h) and query row i < L,
  * over every key j < L, with s_j = <q_i, k_j> / sqrt(d) and W(i) the kept keys:

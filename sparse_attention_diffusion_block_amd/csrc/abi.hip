@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <initializer_list>
+#include <mutex>
 #include <vector>
 
 #include "../../include/rettn.h"
@@ -13,6 +14,28 @@
 namespace {
 
 using rettn::AttnArgs;
+
+// Scratch of the no-allocation entry point: a static device array, one copy per GPU.  Host code
+// never uses the array's name as an address (on the host it is only a stand-in); it uses the
+// device address looked up once per device with hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[RETTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, looked up on its first use (null on failure).
+void* scratch_for_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -89,6 +112,7 @@ const char* rettn_status_str(rettn_status s) {
         case RETTN_EINVAL: return "RETTN_EINVAL: invalid argument";
         case RETTN_EUNSUPPORTED: return "RETTN_EUNSUPPORTED: outside the implemented shapes";
         case RETTN_EHIP: return "RETTN_EHIP: HIP runtime or launch failure";
+        case RETTN_ESCRATCH: return "RETTN_ESCRATCH: request exceeds the static scratch of the no-allocation entry point";
     }
     return "unknown rettn_status";
 }
@@ -167,9 +191,10 @@ rettn_status rettn_dynamic_workspace_bytes(const rettn_desc* desc, size_t* bytes
     return RETTN_OK;
 }
 
-rettn_status rettn_dynamic_index(const rettn_desc* desc, const void* Q, const void* K, int32_t keep, void* workspace,
-                                 size_t workspace_bytes, uint8_t* mask_out, int32_t* row_ptr_out,
-                                 int32_t* col_idx_out, hipStream_t stream) {
+// Validation shared by both dynamic-index entry points; on success *need is the block means' size.
+static rettn_status check_dynamic(const rettn_desc* desc, const void* Q, const void* K, int32_t keep,
+                                  const uint8_t* mask_out, const int32_t* row_ptr_out, const int32_t* col_idx_out,
+                                  size_t* need) {
     if (!desc) return RETTN_EINVAL;
     const int64_t nb = cdiv(desc->L > 0 ? desc->L : 1, desc->block > 0 ? desc->block : 1);
     // the index that the outputs form: its checks are the attention calls' own
@@ -177,20 +202,44 @@ rettn_status rettn_dynamic_index(const rettn_desc* desc, const void* Q, const vo
     idx.nqb = idx.nkb = (int32_t)(nb > 0x7fffffff ? 0 : nb);
     rettn_status st = check_desc(desc, &idx);
     if (st != RETTN_OK) return st;
-    st = check_tensors({Q, K, workspace});
+    st = check_tensors({Q, K});
     if (st != RETTN_OK) return st;
     if (!mask_out || check_words({row_ptr_out, col_idx_out}) != RETTN_OK) return RETTN_EINVAL;
     if (keep < 1) return RETTN_EINVAL;
     if (nb > 2048 || (int64_t)desc->B * desc->H > 65535) return RETTN_EUNSUPPORTED;
-    size_t need = 0;
-    st = rettn_dynamic_workspace_bytes(desc, &need);
-    if (st != RETTN_OK) return st;
-    if (workspace_bytes < need) return RETTN_EINVAL;
+    return rettn_dynamic_workspace_bytes(desc, need);
+}
+
+static rettn_status launch_dynamic(const rettn_desc* desc, const void* Q, const void* K, int32_t keep, float* ws,
+                                   uint8_t* mask_out, int32_t* row_ptr_out, int32_t* col_idx_out,
+                                   hipStream_t stream) {
     const hipError_t e = rettn::launch_dynamic_index(Q, K, desc->dtype == RETTN_BF16, desc->B, desc->H, desc->L,
                                                      desc->d, desc->block, desc->stride_b, desc->stride_h,
-                                                     desc->stride_l, keep, (float*)workspace, mask_out, row_ptr_out,
-                                                     col_idx_out, stream);
+                                                     desc->stride_l, keep, ws, mask_out, row_ptr_out, col_idx_out,
+                                                     stream);
     return e == hipSuccess ? RETTN_OK : RETTN_EHIP;
+}
+
+rettn_status rettn_dynamic_index(const rettn_desc* desc, const void* Q, const void* K, int32_t keep, void* workspace,
+                                 size_t workspace_bytes, uint8_t* mask_out, int32_t* row_ptr_out,
+                                 int32_t* col_idx_out, hipStream_t stream) {
+    size_t need = 0;
+    rettn_status st = check_dynamic(desc, Q, K, keep, mask_out, row_ptr_out, col_idx_out, &need);
+    if (st != RETTN_OK) return st;
+    if (check_tensors({workspace}) != RETTN_OK || workspace_bytes < need) return RETTN_EINVAL;
+    return launch_dynamic(desc, Q, K, keep, (float*)workspace, mask_out, row_ptr_out, col_idx_out, stream);
+}
+
+rettn_status rettn_dynamic_index_noalloc(const rettn_desc* desc, const void* Q, const void* K, int32_t keep,
+                                         uint8_t* mask_out, int32_t* row_ptr_out, int32_t* col_idx_out,
+                                         hipStream_t stream) {
+    size_t need = 0;
+    rettn_status st = check_dynamic(desc, Q, K, keep, mask_out, row_ptr_out, col_idx_out, &need);
+    if (st != RETTN_OK) return st;
+    if (need > RETTN_NOALLOC_SCRATCH_BYTES) return RETTN_ESCRATCH;
+    void* ws = scratch_for_current_device();
+    if (!ws) return RETTN_EHIP;
+    return launch_dynamic(desc, Q, K, keep, (float*)ws, mask_out, row_ptr_out, col_idx_out, stream);
 }
 
 rettn_status rettn_calibrate(const rettn_desc* desc, const void* Q, const void* K, const void* V,

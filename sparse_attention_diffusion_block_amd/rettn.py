@@ -16,7 +16,10 @@ RETTN_F32, RETTN_BF16 = 0, 1
 MASK_DIAG, MASK_BAND, MASK_COGVIDEO3D, MASK_FULL = 0, 1, 2, 3
 RESIDUAL_MASKED, RESIDUAL_DIFFERENCE = 0, 1
 EXPORTED = ("rettn_mask_build", "rettn_index_build", "rettn_index_build_sliced", "rettn_dynamic_workspace_bytes",
-            "rettn_dynamic_index", "rettn_calibrate", "rettn_calibrate_residual", "rettn_sparse", "rettn_status_str")
+            "rettn_dynamic_index", "rettn_dynamic_index_noalloc", "rettn_calibrate", "rettn_calibrate_residual",
+            "rettn_sparse", "rettn_status_str")
+STATUS_ESCRATCH = 4
+NOALLOC_SCRATCH_BYTES = 32 << 20   # RETTN_NOALLOC_SCRATCH_BYTES
 
 
 class Desc(ctypes.Structure):
@@ -69,6 +72,8 @@ def lib():
         L.rettn_dynamic_workspace_bytes.restype = ctypes.c_int
         L.rettn_dynamic_index.argtypes = [ctypes.POINTER(Desc), vp, vp, i32, vp, ctypes.c_size_t, vp, vp, vp, vp]
         L.rettn_dynamic_index.restype = ctypes.c_int
+        L.rettn_dynamic_index_noalloc.argtypes = [ctypes.POINTER(Desc), vp, vp, i32, vp, vp, vp, vp]
+        L.rettn_dynamic_index_noalloc.restype = ctypes.c_int
         L.rettn_calibrate.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, ctypes.POINTER(Index), vp, vp, vp, vp]
         L.rettn_calibrate.restype = ctypes.c_int
         L.rettn_calibrate_residual.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, ctypes.POINTER(Index), vp, vp, vp,
@@ -180,6 +185,26 @@ def dynamic_index(q, k, keep, block, workspace=None, out=None):
                                      workspace.numel() * workspace.element_size(), out.mask.data_ptr(),
                                      out.row_ptr.data_ptr(), out.col_idx.data_ptr(), _stream(q.device)),
            "rettn_dynamic_index")
+    return out
+
+
+def dynamic_index_noalloc(q, k, keep, block, out):
+    """dynamic_index through the entry point that allocates nothing: the block means live in the
+    library's static per-GPU scratch.  `out` (a BlockIndex from dynamic_index of the same shape and
+    keep) receives the result; nothing is allocated here either.  Calls that overlap on one GPU
+    share the scratch and must be ordered by the caller."""
+    if not (q.is_cuda and k.is_cuda and q.dim() == 4 and q.shape == k.shape and q.dtype == k.dtype
+            and q.stride() == k.stride() and q.stride(3) == 1):
+        raise ValueError("Q and K must be CUDA tensors of one [B, H, L, d] layout with d contiguous")
+    B, H, L, d = q.shape
+    nb = -(-L // block)
+    kk = min(int(keep), nb)
+    if out.mask.shape != (B * H, nb, nb) or out.col_stride != nb * kk or out.block != block:
+        raise ValueError("`out` was built for another shape or keep")
+    desc = _desc(q, block)
+    _check(lib().rettn_dynamic_index_noalloc(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), int(keep),
+                                             out.mask.data_ptr(), out.row_ptr.data_ptr(), out.col_idx.data_ptr(),
+                                             _stream(q.device)), "rettn_dynamic_index_noalloc")
     return out
 
 

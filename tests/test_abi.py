@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = rt.lib()
-    for s in range(4):
+    for s in range(5):
         assert lib.rettn_status_str(s).decode().startswith("RETTN_")
 
 
