@@ -13,13 +13,24 @@ The headline value is the sparse step's effective throughput: the flops of
 the kept blocks only (4 d per kept (query, key) pair) divided by the mean
 duration of the sparse-step kernel, measured with HIP events on the stream the
 library launches on, over the timed steps.  ms_per_step is the wall time of
-the whole period.
+the whole period.  `roofline` describes that sparse-step kernel (HBM-bound at
+its arithmetic intensity); `roofline_calibrate` the calibration kernel.
 
-usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+After the timed steps (outside the timed region) the line also carries:
+  sweep_c3        the sparse step on the same shapes under band masks of 75 /
+                  87.5 / 93.8 / 96.9% block sparsity and the video mask, and
+                  the 87.5% -> 96.9% speedup (the pages claim more than 2x);
+  workloads       calibration and sparse-step times of the other workloads
+                  (the image workloads warm and after a 512 MiB cache flush;
+                  the long-video workload at its four windows);
+  cpu_baseline    the CPU oracle's sparse step on the same workload, timed on
+                  the host cores (float32 and float64 modes, a process pool over
+                  (batch, head) slices with one BLAS thread per process).
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
 """
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -31,6 +42,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 matrix peak, TFLOP/s
+POOL_MAX = 16                  # worker processes for the CPU baseline (the host share of one GPU)
 
 
 def log(msg):
@@ -52,32 +64,200 @@ def workload_counts(cfg, mask):
     return f_sparse, f_calib, bytes_alg, pairs
 
 
-def cpu_baseline(cfg, spec, inputs_host, lam, budget_s=20.0):
-    """The CPU oracle's sparse step, timed on whole (batch, head) slices of the same workload."""
-    import oracle
-    from oracle import masks as om
+# ------------------------------------------------------------------ CPU baseline (the oracle)
+_SHARED = {}
+
+
+def _cpu_worker_init(names, meta):
+    """Attach the workload's arrays from shared memory (no copy) and pin BLAS to one thread."""
+    from multiprocessing import shared_memory
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
     except Exception:
-        threads = os.cpu_count() or 1
+        pass
+    for key, name in names.items():
+        shape, dtype = meta[key]
+        shm = shared_memory.SharedMemory(name=name)
+        _SHARED[key] = (shm, np.ndarray(shape, dtype=dtype, buffer=shm.buf))
+
+
+def _cpu_worker(task):
+    """The oracle's sparse step on one (batch, head) slice; returns its compute seconds."""
+    import oracle
+    b, h, block, lam, dtype = task
+    a = {key: val[1] for key, val in _SHARED.items()}
+    sl = (slice(b, b + 1), slice(h, h + 1))
+    t0 = time.perf_counter()
+    oracle.sparse_step(a["q"][sl], a["k"][sl], a["v"][sl], a["mask"], block, a["rho"][sl], a["r"][sl], lam, 1,
+                       dtype=np.dtype(dtype))
+    return time.perf_counter() - t0
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, spec, q, k, v, rho, r, lam):
+    """The CPU oracle's sparse step on every (batch, head) slice of the workload, timed in float32 (the
+    baseline) and float64 (the parity mode): a spawned process pool over the slices, one BLAS thread
+    per process, inputs shared with the workers through shared memory; whole-workload wall time,
+    median of 3 runs (1 if one run exceeds 60 s)."""
+    import multiprocessing as mp
+    from multiprocessing import shared_memory
+    from oracle import masks as om
     mask = om.build_mask(spec.kind, spec.nb, spec.w, spec.text_blocks, spec.tshift)
-    (q, k, v), rho, r = inputs_host
-    heads_done, t_total = 0, 0.0
-    bh_total = cfg.B * cfg.H
-    while heads_done < bh_total and t_total < budget_s:
-        b, h = divmod(heads_done, cfg.H)
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        t0 = time.perf_counter()
-        oracle.sparse_step(q[sl], k[sl], v[sl], mask, cfg.block, rho[sl], r[sl], lam, 1)
-        t_total += time.perf_counter() - t0
-        heads_done += 1
-    f_head, _, _, _ = workload_counts(cfg, mask)
-    f_head /= bh_total
-    return {"value": f_head * heads_done / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"float64 NumPy oracle sparse step on {heads_done} of {bh_total} (batch, head) slices "
-                      f"(all {cfg.L} rows each), {t_total:.1f} s; effective flops of the kept blocks / time"}
+    affinity = len(os.sched_getaffinity(0))
+    workers = max(1, min(affinity, POOL_MAX))
+    f_sparse, _, _, _ = workload_counts(cfg, mask)
+    out = {"unit": "TFLOP/s", "cores": workers, "kind": "oracle", "cpu_model": _cpu_model(),
+           "host_threads_available": affinity}
+    arrays = {"q": q, "k": k, "v": v, "rho": rho, "r": r, "mask": mask}
+    shms, names, meta = [], {}, {}
+    saved_env = {key: os.environ.get(key) for key in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    try:
+        for key, arr in arrays.items():
+            arr = np.ascontiguousarray(arr)
+            shm = shared_memory.SharedMemory(create=True, size=max(arr.nbytes, 1))
+            shms.append(shm)
+            np.ndarray(arr.shape, dtype=arr.dtype, buffer=shm.buf)[...] = arr
+            names[key], meta[key] = shm.name, (arr.shape, arr.dtype.str)
+        for key in saved_env:
+            os.environ[key] = "1"                     # the spawned workers start with one BLAS thread
+        ctx = mp.get_context("spawn")
+        with ctx.Pool(workers, initializer=_cpu_worker_init, initargs=(names, meta)) as pool:
+            for dtype in ("float32", "float64"):
+                tasks = [(b, h, cfg.block, lam, dtype) for b in range(cfg.B) for h in range(cfg.H)]
+                pool.map(_cpu_worker, tasks[:workers], chunksize=1)          # warm the workers (imports)
+                walls = []
+                for _ in range(3):
+                    t0 = time.perf_counter()
+                    pool.map(_cpu_worker, tasks, chunksize=1)
+                    walls.append(time.perf_counter() - t0)
+                    if walls[-1] > 60.0:
+                        break
+                wall = float(np.median(walls))
+                out[dtype] = {"value": round(f_sparse / wall / 1e12, 6), "seconds": round(wall, 3),
+                              "runs": len(walls)}
+    finally:
+        for key, val in saved_env.items():
+            if val is None:
+                os.environ.pop(key, None)
+            else:
+                os.environ[key] = val
+        for shm in shms:
+            shm.close()
+            shm.unlink()
+    out["value"] = out["float32"]["value"]
+    out["sample"] = (f"the oracle's sparse step (float32 mode; float64 beside it) on all {cfg.B * cfg.H} (batch, head) "
+                     f"slices, all {cfg.L} rows each, of the timed workload; {workers} spawned processes with one BLAS "
+                     f"thread each; whole-workload wall time, median of {out['float32']['runs']}; effective flops of "
+                     f"the kept blocks / time")
+    return out
+
+
+# ------------------------------------------------------------------ timed extras (outside the timed region)
+def _gpu_inputs(cfg, seed):
+    """Seeded N(0,1) Q, K, V drawn on the device (timing only: the workload's shapes and distribution)."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    shape = (cfg.B, cfg.H, cfg.L, cfg.d)
+    return tuple((torch.randn(shape, generator=g, device="cuda", dtype=torch.float32) * cfg.input_scale).to(dt)
+                 for _ in range(3))
+
+
+def _sparse_rec(rt, timer, cfg, spec, qkv, rho, r, runs, before=None):
+    from sparse_attention_diffusion_block_amd.measure import _counts
+    import torch
+    m = rt.mask_build(spec.kind, spec.nb, spec.w, spec.text_blocks, spec.tshift)
+    idx = rt.index_build(m, cfg.block)
+    f_sp, _, nbytes, pairs = _counts(cfg, m)
+    out = torch.empty_like(qkv[0])
+    t = timer(lambda: rt.sparse(*qkv, idx, rho, r, lam=cfg.lam, step=1, out=out), runs, before=before)
+    s = t["median_ms"] * 1e-3
+    return {"mask": spec.label(), "token_sparsity": round(1.0 - pairs / (cfg.L * cfg.L), 5), "ms": t["median_ms"],
+            "p10_p90_ms": [t["p10_ms"], t["p90_ms"]], "effective_tflops": round(f_sp / s / 1e12, 1),
+            "algorithmic_gbs": round(nbytes / s / 1e9, 1)}
+
+
+def _calib_rec(rt, timer, cfg, spec, qkv, runs, before=None):
+    from sparse_attention_diffusion_block_amd.measure import _counts
+    import torch
+    m = rt.mask_build(spec.kind, spec.nb, spec.w, spec.text_blocks, spec.tshift)
+    idx = rt.index_build(m, cfg.block)
+    _, f_cal, _, _ = _counts(cfg, m)
+    q = qkv[0]
+    o, rr = torch.empty_like(q), torch.empty_like(q)
+    rho = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    t = timer(lambda: rt.calibrate(*qkv, idx, out=(o, rho, rr)), runs, warm=2 if cfg.number == 5 else 10,
+              before=before)
+    s = t["median_ms"] * 1e-3
+    return {"mask": spec.label(), "ms": t["median_ms"], "tflops": round(f_cal / s / 1e12, 1),
+            "mfma_frac": round(f_cal / s / 1e12 / MFMA_PEAK_TFLOPS, 4)}
+
+
+def extras(rt, c3_sets, rho_c3, r_c3):
+    """Per-workload timings and the density sweep (HIP events, median of batched calls)."""
+    import torch
+    from sparse_attention_diffusion_block_amd.measure import _time
+    from workloads import CONFIGS, SWEEP_C3
+    out = {}
+    cfg3 = CONFIGS[3]
+    log("extras: density sweep on the video workload's shapes")
+    recs = [_sparse_rec(rt, _time, cfg3, spec, c3_sets[1], rho_c3, r_c3, 20) for spec in SWEEP_C3 + cfg3.masks]
+    t875 = recs[1]["ms"]
+    t969 = recs[3]["ms"]
+    out["sweep_c3"] = {"records": recs, "speedup_96.9_over_87.5": round(t875 / t969, 3),
+                       "note": "band windows of 70 / 35 / 17 / 9 of 278 blocks, then the 3D window + text mask; "
+                               "the pages report more than 2x for 87.5% -> 96.9%"}
+    flush = torch.empty(512 << 18, dtype=torch.float32, device="cuda")          # 512 MiB
+    wl = {}
+    for n in (1, 2, 4, 5):
+        cfg = CONFIGS[n]
+        log(f"extras: workload {n} ({cfg.name})")
+        qkv = _gpu_inputs(cfg, 100 + n)
+        qkv2 = _gpu_inputs(cfg, 200 + n)
+        g = torch.Generator(device="cuda")
+        g.manual_seed(300 + n)
+        rho = torch.rand(qkv[0].shape[:3], generator=g, device="cuda") * 0.98 + 0.01
+        r = (torch.randn(qkv[0].shape, generator=g, device="cuda") * 0.05).to(qkv[0].dtype)
+        timings = [("warm", None)] + ([("cold", lambda: flush.zero_())] if n in (2, 4) else [])
+        runs = 5 if n == 5 else 20
+        rec = {"shape": f"B={cfg.B} H={cfg.H} L={cfg.L} d={cfg.d} block={cfg.block} {cfg.dtype}", "masks": []}
+        for spec in cfg.masks:
+            m = {"mask": spec.label()}
+            for label, before in timings:
+                if n != 5 or spec is cfg.masks[0]:
+                    m[f"calibrate_{label}"] = _calib_rec(rt, _time, cfg, spec, qkv, 3 if n == 5 else runs, before)
+                m[f"sparse_{label}"] = _sparse_rec(rt, _time, cfg, spec, qkv2, rho, r, runs, before)
+            rec["masks"].append(m)
+        wl[cfg.name] = rec
+        del qkv, qkv2, rho, r
+        torch.cuda.empty_cache()
+    out["workloads"] = wl
+    out["extras_note"] = ("HIP events around 5 back-to-back calls (one more queued in front), median of the samples; "
+                          "cold: a 512 MiB buffer is written before every single call; inputs drawn on the device "
+                          "with the workloads' shapes and N(0,1) values")
+    return out
+
+
+def copy_bandwidth():
+    """Measured read + write rate of a plain 1 GiB device copy (the streaming ceiling of this chip)."""
+    import torch
+    from sparse_attention_diffusion_block_amd.measure import _time
+    x = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    t = _time(lambda: y.copy_(x), 10)
+    return 2.0 * (1 << 30) / (t["median_ms"] * 1e-3) / 1e9
 
 
 def main():
@@ -87,6 +267,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter scale reference) and exit")
     args = ap.parse_args()
@@ -112,7 +293,8 @@ def main():
         return 0
 
     import sparse_attention_diffusion_block_amd as rt
-    from workloads import CONFIGS, drift, make_qkv
+    from sparse_attention_diffusion_block_amd.profiling import dispatched_kernels, kernel_source_hash, read_traffic
+    from workloads import CONFIGS, drift, make_cache, make_qkv
 
     cfg = CONFIGS[args.config]
     spec = cfg.masks[0]
@@ -127,7 +309,7 @@ def main():
         host_sets.append(drift(*host_sets[-1], cfg.number, kstep, sigma=cfg.drift_sigma, scale=cfg.input_scale,
                                dtype=cfg.dtype))
     dev_sets = [tuple(torch.from_numpy(x).to("cuda").to(dt) for x in s) for s in host_sets]
-    host_keep = host_sets[:2] if not args.no_cpu_baseline else None
+    host_keep = host_sets[1] if not args.no_cpu_baseline else None
     del host_sets
 
     B, H, L, d = cfg.B, cfg.H, cfg.L, cfg.d
@@ -193,11 +375,10 @@ def main():
     sparse_tflops = f_sparse / t_sp / 1e12
     calib_tflops = f_calib / t_cal / 1e12
     sparse_gbs = bytes_alg / t_sp / 1e9
-    calib_gbs = bytes_alg / t_cal / 1e9
     ai_sparse = f_sparse / bytes_alg
     ridge = MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    copy_gbs = copy_bandwidth()
 
-    from sparse_attention_diffusion_block_amd.profiling import kernel_source_hash, read_traffic
     traffic = read_traffic(os.path.join(ROOT, "profiles", f"hbm_traffic_{cfg.name}.txt"))
 
     def traffic_of(kernel):
@@ -205,22 +386,23 @@ def main():
         sha, nbytes = traffic.get(kernel, (None, None))
         return nbytes if sha is not None and sha == kernel_source_hash(kernel) else None
 
-    k_sparse, k_cal = "sparse64_kernel<64>", "calib_kernel<64, 64>"
-    roof_sparse = {"bound": "hbm" if ai_sparse < ridge else "mfma",
+    k_cal, k_sparse = dispatched_kernels(cfg.dtype, cfg.block, cfg.d, cfg.L)
+    hbm_bound = ai_sparse < ridge
+    roof_sparse = {"bound": "hbm" if hbm_bound else "mfma",
                    "kernel": k_sparse,
-                   "achieved": round(sparse_gbs, 1) if ai_sparse < ridge else round(sparse_tflops, 1),
-                   "peak": HBM_PEAK_GBS if ai_sparse < ridge else MFMA_PEAK_TFLOPS,
-                   "unit": "GB/s" if ai_sparse < ridge else "TFLOP/s",
+                   "achieved": round(sparse_gbs, 1) if hbm_bound else round(sparse_tflops, 1),
+                   "peak": HBM_PEAK_GBS if hbm_bound else MFMA_PEAK_TFLOPS,
+                   "unit": "GB/s" if hbm_bound else "TFLOP/s",
                    "traffic": traffic_of(k_sparse),
                    "mfma_frac": round(sparse_tflops / MFMA_PEAK_TFLOPS, 4),
+                   "measured_copy_gbs": round(copy_gbs, 1),
+                   "frac_of_measured_copy": round(sparse_gbs / copy_gbs, 4),
                    "ms": round(t_sp * 1e3, 4)}
     roof_sparse["frac"] = round(roof_sparse["achieved"] / roof_sparse["peak"], 4)
     roof_cal = {"bound": "mfma", "kernel": k_cal,
                 "achieved": round(calib_tflops, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(calib_tflops / MFMA_PEAK_TFLOPS, 4), "traffic": traffic_of(k_cal),
                 "ms": round(t_cal * 1e3, 4)}
-    # the dominant kernel of a step is the one with the larger share of its time
-    dominant_is_cal = t_cal > T * t_sp
     out = {
         "metric": "sparse-step ms + effective TFLOP/s at 96.9% sparsity, L=17776, H=30, d=64",
         "value": round(sparse_tflops, 2),
@@ -237,6 +419,8 @@ def main():
         "config": {"workload": f"{cfg.name}: B={B} H={H} L={L} d={d} block={cfg.block}, "
                                f"mask {spec.label()} ({1 - pairs / (L * L):.4%} sparsity), "
                                f"1 calibration + {T} sparse steps per step, lambda={lam}",
+                   "precision": "bf16 I/O, bf16 QK^T, fp16 P*V, fp32 accumulation and softmax" if cfg.dtype == "bf16"
+                                else "fp32 throughout",
                    "global_batch": B, "seq_len": L, "parallelism": "none (1 GPU)"},
         "sparse_step_ms": round(t_sp * 1e3, 4),
         "sparse_step_ms_p10_p50_p90": [round(float(np.percentile(sp_each, q)), 4) for q in (10, 50, 90)],
@@ -247,15 +431,16 @@ def main():
         "sparse_effective_flops": f_sparse,
         "calibrate_flops": f_calib,
         "algorithmic_bytes_per_launch": bytes_alg,
-        "roofline": roof_cal if dominant_is_cal else roof_sparse,
-        "roofline_sparse": roof_sparse,
+        "roofline": roof_sparse,
         "roofline_calibrate": roof_cal,
     }
+    if not args.no_extras and args.config == 3:
+        out.update(extras(rt, dev_sets, rho, r_cal))
     if not args.no_cpu_baseline:
-        from workloads import make_cache
         rho_c, r_c = make_cache(B, H, L, d, seed=cfg.number, dtype=cfg.dtype)
-        log("timing the CPU oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(cfg, spec, (host_keep[1], rho_c, r_c), lam)
+        log("timing the CPU oracle (float32 and float64 modes)")
+        q1, k1, v1 = host_keep
+        out["cpu_baseline"] = cpu_baseline(cfg, spec, q1, k1, v1, rho_c, r_c, lam)
     print(json.dumps(out))
     return 0
 

@@ -122,16 +122,17 @@ def calibrate(q, k, v, mask, block, rows=None):
     return o, rho, r
 
 
-def window_attention(q, k, v, mask, block, rows=None):
+def window_attention(q, k, v, mask, block, rows=None, dtype=np.float64):
     """Plain sparse attention: softmax over the kept keys only (pre-softmax masking).
 
-    Rows whose window is empty give zeros.  Also returns the window mass D'
-    is not needed by callers; only the normalised output is returned.
+    Rows whose window is empty give zeros; only the normalised output is
+    returned.  `dtype` is the arithmetic type: float64 (parity) or float32
+    (the same steps timed in single precision as a CPU baseline).
     """
-    q, k, v = _as64(q), _as64(k), _as64(v)
+    q, k, v = (np.asarray(x, dtype=dtype) for x in (q, k, v))
     B, H, L, d = q.shape
     rows = np.arange(L) if rows is None else np.asarray(rows, dtype=np.int64)
-    out = np.zeros((B, H, len(rows), d))
+    out = np.zeros((B, H, len(rows), d), dtype=dtype)
     t = tau(d)
     groups = _rows_by_block(rows, block)
     for b in range(B):
@@ -149,18 +150,19 @@ def window_attention(q, k, v, mask, block, rows=None):
     return out
 
 
-def sparse_step(q, k, v, mask, block, rho, r, lam, step, rows=None):
+def sparse_step(q, k, v, mask, block, rho, r, lam, step, rows=None, dtype=np.float64):
     """Sparse step k after a calibration (Re-ttention's statistical reshape).
 
     Over the kept keys W(i) only:
         s'_j = tau <q'_i, k'_j>, m' = max_W s', e'_j = exp(s'_j - m'), D' = sum_W e'
         O'_i = min(1, rho_i (1 + lambda k)) * sum_W e'_j v'_j / D' + R_i
     and O'_i = R_i when W(i) is empty.  `rho` [B,H,n] and `r` [B,H,n,d] are
-    the cached values for the requested rows, in the same order.
+    the cached values for the requested rows, in the same order.  `dtype` as
+    in window_attention.
     """
-    o_sp = window_attention(q, k, v, mask, block, rows)
-    rho = _as64(rho)
-    r = _as64(r)
+    o_sp = window_attention(q, k, v, mask, block, rows, dtype=dtype)
+    rho = np.asarray(rho, dtype=dtype)
+    r = np.asarray(r, dtype=dtype)
     B, H, L, _ = np.asarray(q).shape
     rows_arr = np.arange(L) if rows is None else np.asarray(rows, dtype=np.int64)
     nonempty = np.zeros((B, H, len(rows_arr)))
@@ -168,7 +170,7 @@ def sparse_step(q, k, v, mask, block, rho, r, lam, step, rows=None):
         for h in range(H):
             m_bh = slice_mask(mask, b, h, B, H)
             nonempty[b, h] = [bool(m_bh[int(i) // block].any()) for i in rows_arr]
-    scale = ramp(rho, lam, step) * nonempty
+    scale = (ramp(rho, lam, step) * nonempty).astype(dtype)
     return scale[..., None] * o_sp + r
 
 

@@ -5,6 +5,7 @@
     python -m sparse_attention_diffusion_block_amd.measure peaks
     python -m sparse_attention_diffusion_block_amd.measure dynamic  [--runs 50] [--keep 9]
     python -m sparse_attention_diffusion_block_amd.measure graph    [--runs 50]
+    python -m sparse_attention_diffusion_block_amd.measure kernels  --config N [--runs 3]
 
 sweep    the sparse step on the shapes of the CogVideoX-2B-like workload (B=2, H=30,
          L=17776, d=64, block 64) under band windows of 75 / 87.5 / 93.8 / 96.9% block
@@ -20,6 +21,8 @@ dynamic  on the CogVideoX-2B-like shapes: the dynamic block-mask index (block me
 graph    wall time of one refresh period (a calibration and the sparse steps until the next
          one, outputs preallocated) on the image and video workloads, launched eagerly from
          Python and replayed from a HIP graph: what the host's launch path costs per period.
+kernels  the calibration and the sparse step of one workload (every mask), `--runs` calls
+         each, nothing timed: the program a counter-collecting profiler runs.
 peaks    a measured matrix peak (a large bfloat16 GEMM through the vendor library) and
          a measured copy bandwidth, beside the datasheet figures.
 
@@ -258,6 +261,25 @@ def cmd_graph(args):
         torch.cuda.empty_cache()
 
 
+def cmd_kernels(args):
+    import torch
+    from workloads import CONFIGS
+    from . import rettn as rt
+    cfg = CONFIGS[args.config]
+    base, drifted, rho, r = _inputs(cfg)
+    q, k, v = base
+    o, rh, rr, o2 = torch.empty_like(q), torch.empty_like(rho), torch.empty_like(q), torch.empty_like(q)
+    for spec in cfg.masks:
+        idx = rt.index_build(rt.mask_build(spec.kind, spec.nb, spec.w, spec.text_blocks, spec.tshift), cfg.block)
+        for _ in range(args.runs):
+            rt.calibrate(q, k, v, idx, out=(o, rh, rr))
+        for _ in range(args.runs):
+            rt.sparse(*drifted, idx, rho, r, lam=cfg.lam, step=1, out=o2)
+        torch.cuda.synchronize()
+        print(json.dumps({"what": "kernels", "workload": cfg.name, "mask": spec.label(), "calls": args.runs}),
+              flush=True)
+
+
 def cmd_peaks(args):
     import torch
     n = 8192
@@ -280,9 +302,11 @@ def cmd_peaks(args):
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
-    for name in ("sweep", "configs", "peaks", "dynamic", "graph"):
+    for name in ("sweep", "configs", "peaks", "dynamic", "graph", "kernels"):
         sp = sub.add_parser(name)
-        sp.add_argument("--runs", type=int, default=50)
+        sp.add_argument("--runs", type=int, default=3 if name == "kernels" else 50)
+        if name == "kernels":
+            sp.add_argument("--config", type=int, required=True)
         if name == "dynamic":
             sp.add_argument("--keep", type=int, default=9)
     args = ap.parse_args(argv)
@@ -293,7 +317,7 @@ def main(argv=None):
     from . import rettn
     rettn.lib()
     return {"sweep": cmd_sweep, "configs": cmd_configs, "peaks": cmd_peaks, "dynamic": cmd_dynamic,
-            "graph": cmd_graph}[args.cmd](args) or 0
+            "graph": cmd_graph, "kernels": cmd_kernels}[args.cmd](args) or 0
 
 
 if __name__ == "__main__":

@@ -3,12 +3,15 @@
     python -m sparse_attention_diffusion_block_amd.profiling stats KERNEL_STATS_CSV --command "..."
     python -m sparse_attention_diffusion_block_amd.profiling traffic --fetch CSV --write CSV \\
         --copy-fetch CSV --copy-write CSV --copy-bytes N --command "..."
+    python -m sparse_attention_diffusion_block_amd.profiling counters CSV [CSV ...] --command "..."
 
 `stats` condenses a `--kernel-trace --stats` kernel-statistics CSV.  `traffic`
 turns FETCH_SIZE / WRITE_SIZE counter CSVs (KiB per dispatch) into HBM bytes
 per launch, each scaled by what the same counter reads for a plain device copy
 of known size, and records the hash of each kernel's source so that a reader
 (the bench) can tell whether the counters still describe the current kernel.
+`counters` tabulates SQ / GRBM counters (one CSV per collection pass) as the
+mean per dispatch of each kernel, with the utilisations derived from them.
 """
 import argparse
 import collections
@@ -30,6 +33,31 @@ KERNEL_SOURCES = {
     "dyn_topk_kernel": ["dynamic.hip", "common.h", "attn.h"],
     "index_": ["index.hip", "common.h", "attn.h"],
 }
+
+
+def _pad_d(d):
+    return 32 if d <= 32 else 64 if d <= 64 else 96 if d <= 96 else 128
+
+
+def dispatched_kernels(dtype, block, d, L, stride_l=None):
+    """(calibration kernel, sparse-step kernel) that the library launches for contiguous
+    [B, H, L, d] tensors (row pitch stride_l, default d), named as rocprofv3 reports them in short
+    form.  Follows the dispatch of the bf16 and fp32 launchers: the fast kernels take a slice only if
+    its 32-bit buffer offsets cannot wrap (rows rounded up to 256, times the pitch in bytes, at most
+    2^31 - 256)."""
+    sl = d if stride_l is None else stride_l
+    fits = -(-L // 256) * 256 * sl * 2 <= (1 << 31) - 256
+    dp = _pad_d(d)
+    if dtype == "f32":
+        return f"attn_f32_kernel<{block}, {dp}, true>", f"attn_f32_kernel<{block}, {dp}, false>"
+    cal = f"calib_kernel<{block}, {dp}>" if block in (64, 128) and fits else f"attn_bf16_kernel<{block}, {dp}, true>"
+    if block == 64 and d <= 64 and fits:
+        sp = f"sparse64_kernel<{dp}>"
+    elif (block == 128 or (block == 64 and d > 64)) and fits:
+        sp = f"sparse_wg_kernel<{block}, {(96 if dp <= 96 else 128) if block == 64 else dp}>"
+    else:
+        sp = f"attn_bf16_kernel<{block}, {dp}, false>"
+    return cal, sp
 
 
 def kernel_source_hash(kernel):
@@ -97,6 +125,64 @@ def cmd_traffic(args):
         print(f"{short_name(k)} | {sha} | {fetch[k]:.1f} | {write[k]:.1f} | {fb:.0f} | {wb:.0f} | {fb + wb:.0f}")
 
 
+# SIMDs and compute units of the chip (MI355X: 256 CUs of 4 SIMDs)
+CU_NUM, SIMD_NUM = 256, 1024
+
+
+def _all_counter_means(path):
+    """{kernel: {counter: mean value per dispatch}} over every counter in one CSV."""
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in _rows(path):
+        acc[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in acc.items()}
+
+
+def derived(c):
+    """Utilisations from raw counters, with the definitions rocprofv3 documents for its derived
+    metrics.  GRBM_GUI_ACTIVE is summed over the 8 XCDs, so one XCD's active cycles are 1/8 of it.
+    Missing inputs give no entry."""
+    out = {}
+    gui = c.get("GRBM_GUI_ACTIVE")
+    if not gui:
+        return out
+    cyc = gui / 8.0                                       # busy cycles of the GPU
+    out["gpu_cycles"] = cyc
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+        out["mfma_busy_pct"] = 100.0 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * SIMD_NUM)
+    if "SQ_ACTIVE_INST_VALU" in c:                        # quad-cycles, per SE sum
+        out["valu_busy_pct"] = 100.0 * 4 * c["SQ_ACTIVE_INST_VALU"] / (cyc * SIMD_NUM)
+    if "SQ_VALU_MFMA_COEXEC_CYCLES" in c and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+        out["coexec_pct_of_mfma_busy"] = 100.0 * c["SQ_VALU_MFMA_COEXEC_CYCLES"] / max(c["SQ_VALU_MFMA_BUSY_CYCLES"], 1)
+    if "SQ_WAVE_CYCLES" in c:                             # quad-cycles: resident waves per SIMD
+        out["waves_per_simd"] = 4 * c["SQ_WAVE_CYCLES"] / (cyc * SIMD_NUM)
+    if "SQ_LDS_BANK_CONFLICT" in c and "SQ_LDS_IDX_ACTIVE" in c:
+        out["lds_bank_conflict_pct_of_active"] = 100.0 * c["SQ_LDS_BANK_CONFLICT"] / max(c["SQ_LDS_IDX_ACTIVE"], 1)
+    if "SQ_LDS_IDX_ACTIVE" in c:
+        out["lds_active_pct"] = 100.0 * c["SQ_LDS_IDX_ACTIVE"] / (cyc * CU_NUM)
+    if "SQ_INSTS_VALU" in c and "SQ_WAVES" in c:
+        out["valu_insts_per_wave"] = c["SQ_INSTS_VALU"] / c["SQ_WAVES"]
+    if "SQ_INSTS_MFMA" in c and "SQ_WAVES" in c:
+        out["mfma_insts_per_wave"] = c["SQ_INSTS_MFMA"] / c["SQ_WAVES"]
+    return out
+
+
+def cmd_counters(args):
+    merged = collections.defaultdict(dict)
+    for path in args.csv:
+        for k, cs in _all_counter_means(path).items():
+            merged[k].update(cs)
+    print(f"# rocprofv3 counters, mean per dispatch (one collection pass per CSV)\n# command: {args.command}")
+    for k in sorted(merged):
+        if kernel_source_hash(k) is None:
+            continue
+        c = merged[k]
+        print(f"\n## {short_name(k)} | source_sha256 {kernel_source_hash(k)}")
+        for name in sorted(c):
+            print(f"{name:34s} {c[name]:18.1f}")
+        for name, val in derived(c).items():
+            print(f"{'= ' + name:34s} {val:18.2f}")
+
+
 def read_traffic(path):
     """{kernel short name: (source sha, traffic bytes)} from a `traffic` summary."""
     out = {}
@@ -123,8 +209,11 @@ def main(argv=None):
         t.add_argument(a, required=True)
     t.add_argument("--copy-bytes", type=float, required=True)
     t.add_argument("--command", default="")
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+")
+    c.add_argument("--command", default="")
     args = ap.parse_args(argv)
-    (cmd_stats if args.cmd == "stats" else cmd_traffic)(args)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters}[args.cmd](args)
 
 
 if __name__ == "__main__":
