@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librettn.so")
-SOURCES = ["abi.hip", "attn_bf16.hip", "attn_f32.hip", "index.hip", "sparse64.hip", "calib.hip", "dynamic.hip", "sparse_wg.hip"]
+SOURCES = ["host.cpp", "abi.hip", "attn_bf16.hip", "attn_f32.hip", "index.hip", "sparse64.hip", "calib.hip", "dynamic.hip", "sparse_wg.hip"]
 ARCH = "gfx950"
 # Packed fp32 instructions are disabled in all device code.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
@@ -39,7 +39,7 @@ def build(verbose=False):
     """Compile every HIP source and link librettn.so; always rebuilds."""
     hipcc = _hipcc()
     os.makedirs(OBJ, exist_ok=True)
-    objs = [os.path.join(OBJ, s.replace(".hip", ".o")) for s in SOURCES]
+    objs = [os.path.join(OBJ, os.path.splitext(s)[0] + ".o") for s in SOURCES]
     cmds = [[hipcc, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
     with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as ex:
         for out in ex.map(_run, cmds):
@@ -47,8 +47,21 @@ def build(verbose=False):
                 print(out)
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    _check_launch_stubs(tmp)
     os.replace(tmp, LIB)
     return LIB
+
+
+def _check_launch_stubs(path):
+    """Fail the build if a kernel's host launch stub is missing.  The host pass of hipcc has been
+    seen to skip emitting a stub, for some arrangements of lambdas and arrays in a kernel body,
+    without any diagnostic; the library then links and only fails when it is loaded."""
+    nm = shutil.which("nm") or "/opt/rocm/llvm/bin/llvm-nm"
+    p = subprocess.run([nm, "-D", "--undefined-only", path], stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                       text=True)
+    missing = [l.split()[-1] for l in p.stdout.splitlines() if "__device_stub__" in l]
+    if missing:
+        raise RuntimeError(f"{path}: kernel launch stubs missing from the host code: {missing[:4]}")
 
 
 if __name__ == "__main__":

@@ -113,25 +113,40 @@ __global__ void __launch_bounds__(CalCfg<DP>::NT, CalCfg<DP>::WPS) calib_kernel(
     // (plain expressions only inside these lambdas: see the note in sparse64.hip)
     const int nkt = (a.L + 63) / 64;
     u32x4 vreg[C::VC];
+    // A lane's byte offset within a tile is the same for every tile (a padded chunk takes an offset
+    // past every record); the tile's row offset kt * 64 * row_bytes rides in the scalar offset.
+    // (Each offset array is declared right before the lambda that reads it: other placements
+    // kept the host compiler from emitting the launch stubs.)
+    uint32_t k_off[C::KL];
+#pragma unroll
+    for (int j = 0; j < C::KL; ++j) {
+        const int piece = wave + j * C::NW;                  // 1 KiB piece of the tile
+        const int r = piece * (64 / C::CPR) + lane / C::CPR; // key row within the tile
+        const int c = (lane % C::CPR) ^ swz(r);              // logical chunk loaded into this slot
+        k_off[j] = c * 8 < a.d ? (uint32_t)r * row_bytes + 16u * c : kOOB;
+    }
     auto issue_k = [&](int kt, int buf) {
 #pragma unroll
         for (int j = 0; j < C::KL; ++j) {
-            const int piece = wave + j * C::NW;                  // 1 KiB piece of the tile
-            const int r = piece * (64 / C::CPR) + lane / C::CPR; // key row within the tile
-            const int c = (lane % C::CPR) ^ swz(r);              // logical chunk loaded into this slot
-            const uint32_t off = c * 8 < a.d ? (uint32_t)(kt * 64 + r) * row_bytes + 16u * c : kOOB;
+            const int piece = wave + j * C::NW;
+            const uint32_t off = k_off[j];
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rk, (__attribute__((address_space(3))) void*)(lds + buf * 2 * C::TILE + piece * 512), 16, off, 0, 0, 0);
+                rk, (__attribute__((address_space(3))) void*)(lds + buf * 2 * C::TILE + piece * 512), 16, off,
+                (uint32_t)kt * 64u * row_bytes, 0, 0);
         }
     };
+    uint32_t v_off[C::VC];
+#pragma unroll
+    for (int j = 0; j < C::VC; ++j) {
+        const int id = tid + j * C::NT;
+        const int r = id / C::CPR;
+        const int c = (id % C::CPR) ^ swz(r);
+        v_off[j] = c * 8 < a.d ? (uint32_t)r * row_bytes + 16u * c : kOOB;
+    }
     auto issue_v = [&](int kt) {
 #pragma unroll
         for (int j = 0; j < C::VC; ++j) {
-            const int id = tid + j * C::NT;
-            const int r = id / C::CPR;
-            const int c = (id % C::CPR) ^ swz(r);
-            const uint32_t off = c * 8 < a.d ? (uint32_t)(kt * 64 + r) * row_bytes + 16u * c : kOOB;
-            vreg[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+            vreg[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, v_off[j], (uint32_t)kt * 64u * row_bytes, 0));
         }
     };
     auto store_v = [&](int buf) {
@@ -169,14 +184,14 @@ __global__ void __launch_bounds__(CalCfg<DP>::NT, CalCfg<DP>::WPS) calib_kernel(
         const uint16_t* vs = ks + C::TILE;
         if constexpr (C::QLDS) asm volatile("" : "+v"(qoff));   // re-read Q every tile, not kept in registers
 
-        // S^T for the tile's two 32-key halves
+        // S^T for the tile's two 32-key halves: two independent MFMA chains, issued alternately
         f32x16 sacc[2];
+        sacc[0] = sacc[1] = f32x16{};
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            sacc[kt] = f32x16{};
-            const uint16_t* kr = ks + (kt * 32 + n) * C::RS;
+        for (int s = 0; s < C::NS; ++s) {
 #pragma unroll
-            for (int s = 0; s < C::NS; ++s) {
+            for (int kt = 0; kt < 2; ++kt) {
+                const uint16_t* kr = ks + (kt * 32 + n) * C::RS;
                 const u32x4 w = *(const u32x4*)(kr + (((2 * s + h) ^ swn) << 3));
                 u32x4 qv;
                 if constexpr (C::QLDS) qv = *(const u32x4*)(qlds + qoff + (((2 * s + h) ^ swn) << 3));

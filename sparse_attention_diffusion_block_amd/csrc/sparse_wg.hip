@@ -107,26 +107,41 @@ sparse_wg_kernel(const AttnArgs a) {
 
     // Tile staging.  K: direct-to-LDS, wave w fills 1 KiB pieces w, w + NW, ...; lane -> (row, physical chunk).
     // V: thread t holds 16-byte chunks t, t + NT, ... in registers until they are re-encoded and stored.
+    // A lane's byte offset within a tile is the same for every tile (a padded chunk takes an offset
+    // past every record); the tile's row offset k0 * row_bytes rides in the scalar offset.  (Each
+    // offset array is declared right before the lambda that reads it: other placements kept the
+    // host compiler from emitting the launch stubs.)
     u32x4 vreg[C::VC];
+    uint32_t k_off[C::KL];
+#pragma unroll
+    for (int j = 0; j < C::KL; ++j) {
+        const int piece = wave + j * C::NW;
+        const int r = piece * (64 / C::CPR) + lane / C::CPR;
+        const int c = (lane % C::CPR) ^ swz(r);
+        k_off[j] = c * 8 < a.d ? (uint32_t)r * row_bytes + 16u * c : kOOB;
+    }
     auto issue_k = [&](int k0, int buf) {
 #pragma unroll
         for (int j = 0; j < C::KL; ++j) {
             const int piece = wave + j * C::NW;
-            const int r = piece * (64 / C::CPR) + lane / C::CPR;
-            const int c = (lane % C::CPR) ^ swz(r);
-            const uint32_t off = c * 8 < a.d ? (uint32_t)(k0 + r) * row_bytes + 16u * c : kOOB;
+            const uint32_t off = k_off[j];
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rk, (__attribute__((address_space(3))) void*)(lds + buf * 2 * C::TILE + piece * 512), 16, off, 0, 0, 0);
+                rk, (__attribute__((address_space(3))) void*)(lds + buf * 2 * C::TILE + piece * 512), 16, off,
+                (uint32_t)k0 * row_bytes, 0, 0);
         }
     };
+    uint32_t v_off[C::VC];
+#pragma unroll
+    for (int j = 0; j < C::VC; ++j) {
+        const int id = tid + j * C::NT;
+        const int r = id / C::CPR;
+        const int c = (id % C::CPR) ^ swz(r);
+        v_off[j] = c * 8 < a.d ? (uint32_t)r * row_bytes + 16u * c : kOOB;
+    }
     auto issue_v = [&](int k0) {
 #pragma unroll
         for (int j = 0; j < C::VC; ++j) {
-            const int id = tid + j * C::NT;
-            const int r = id / C::CPR;
-            const int c = (id % C::CPR) ^ swz(r);
-            const uint32_t off = c * 8 < a.d ? (uint32_t)(k0 + r) * row_bytes + 16u * c : kOOB;
-            vreg[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+            vreg[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, v_off[j], (uint32_t)k0 * row_bytes, 0));
         }
     };
     auto store_v = [&](int buf) {

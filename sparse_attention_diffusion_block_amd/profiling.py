@@ -24,14 +24,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 # kernel symbol fragment -> source files that define it
 KERNEL_SOURCES = {
-    "sparse64_kernel": ["sparse64.hip", "common.h", "attn.h"],
-    "calib_kernel": ["calib.hip", "common.h", "attn.h"],
-    "attn_bf16_kernel": ["attn_bf16.hip", "common.h", "attn.h"],
-    "attn_f32_kernel": ["attn_f32.hip", "common.h", "attn.h"],
-    "sparse_wg_kernel": ["sparse_wg.hip", "common.h", "attn.h"],
-    "dyn_pool_kernel": ["dynamic.hip", "common.h", "attn.h"],
-    "dyn_topk_kernel": ["dynamic.hip", "common.h", "attn.h"],
-    "index_": ["index.hip", "common.h", "attn.h"],
+    "sparse64_kernel": ["sparse64.hip", "common.h", "attn.h", "args.h"],
+    "calib_kernel": ["calib.hip", "common.h", "attn.h", "args.h"],
+    "attn_bf16_kernel": ["attn_bf16.hip", "common.h", "attn.h", "args.h"],
+    "attn_f32_kernel": ["attn_f32.hip", "common.h", "attn.h", "args.h"],
+    "sparse_wg_kernel": ["sparse_wg.hip", "common.h", "attn.h", "args.h"],
+    "dyn_pool_kernel": ["dynamic.hip", "common.h", "attn.h", "args.h"],
+    "dyn_topk_kernel": ["dynamic.hip", "common.h", "attn.h", "args.h"],
+    "index_": ["index.hip", "common.h", "attn.h", "args.h"],
 }
 
 
