@@ -306,7 +306,7 @@ def main():
     log(f"generating inputs for {cfg.name} (B={cfg.B}, H={cfg.H}, L={cfg.L}, d={cfg.d})")
     host_sets = [make_qkv(cfg.B, cfg.H, cfg.L, cfg.d, cfg.seed, scale=cfg.input_scale, dtype=cfg.dtype)]
     for kstep in range(1, T + 1):
-        host_sets.append(drift(*host_sets[-1], cfg.number, kstep, sigma=cfg.drift_sigma, scale=cfg.input_scale,
+        host_sets.append(drift(*host_sets[-1], cfg.number, kstep, sigma=cfg.drift_sigma,
                                dtype=cfg.dtype))
     dev_sets = [tuple(torch.from_numpy(x).to("cuda").to(dt) for x in s) for s in host_sets]
     host_keep = host_sets[1] if not args.no_cpu_baseline else None

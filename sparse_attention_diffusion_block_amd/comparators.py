@@ -89,7 +89,7 @@ def compare_chain(config=3, T=5, steps=10, sigma=None, lam=None, mask_index=0, l
     records = []
     for t in range(steps):
         if t > 0:
-            host = drift(*host, cfg.number, t, sigma=sigma, scale=cfg.input_scale, dtype=cfg.dtype)
+            host = drift(*host, cfg.number, t, sigma=sigma, dtype=cfg.dtype)
         q, k, v = (torch.from_numpy(x).to("cuda").to(dt) for x in host)
         full, rho_t, r_t = rt.calibrate(q, k, v, idx)
         kstep = t % T

@@ -94,7 +94,7 @@ def _inputs(cfg):
     from workloads import drift, make_cache, make_qkv
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     q, k, v = make_qkv(cfg.B, cfg.H, cfg.L, cfg.d, cfg.seed, scale=cfg.input_scale, dtype=cfg.dtype)
-    q2, k2, v2 = drift(q, k, v, cfg.number, 1, sigma=cfg.drift_sigma, scale=cfg.input_scale, dtype=cfg.dtype)
+    q2, k2, v2 = drift(q, k, v, cfg.number, 1, sigma=cfg.drift_sigma, dtype=cfg.dtype)
     rho, r = make_cache(cfg.B, cfg.H, cfg.L, cfg.d, seed=cfg.number, dtype=cfg.dtype)
     on = lambda x: torch.from_numpy(x).to("cuda").to(dt)
     return (on(q), on(k), on(v)), (on(q2), on(k2), on(v2)), torch.from_numpy(rho).to("cuda"), on(r)
@@ -219,7 +219,7 @@ def cmd_graph(args):
         dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
         sets = [make_qkv(cfg.B, cfg.H, cfg.L, cfg.d, cfg.seed, scale=cfg.input_scale, dtype=cfg.dtype)]
         for kstep in range(1, T + 1):
-            sets.append(drift(*sets[-1], cfg.number, kstep, sigma=cfg.drift_sigma, scale=cfg.input_scale,
+            sets.append(drift(*sets[-1], cfg.number, kstep, sigma=cfg.drift_sigma,
                               dtype=cfg.dtype))
         dev = [tuple(torch.from_numpy(x).to("cuda").to(dt) for x in st) for st in sets]
         del sets

@@ -170,7 +170,7 @@ def chained_drift_run(config: int = 3, T: int = 5, steps: int = 15, layers: int 
     for t in range(steps):
         for j in range(layers):
             if t > 0:
-                host[j] = drift(*host[j], cfg.number + 100 * j, t, sigma=sigma, scale=cfg.input_scale, dtype=cfg.dtype)
+                host[j] = drift(*host[j], cfg.number + 100 * j, t, sigma=sigma, dtype=cfg.dtype)
             q, k, v = (torch.from_numpy(x).to("cuda").to(dt) for x in host[j])
             o = runs[j](t, q, k, v)
             rt.calibrate(q, k, v, idx, out=(full_o, full_rho, full_r))
@@ -218,7 +218,7 @@ def dynamic_mask_run(config: int = 3, T: int = 5, steps: int = 10, keep: Optiona
         rho_c = r_c = idx_c = None
         for t in range(steps):
             if t > 0:
-                host = drift(*host, cfg.number, t, sigma=sigma, scale=cfg.input_scale, dtype=cfg.dtype)
+                host = drift(*host, cfg.number, t, sigma=sigma, dtype=cfg.dtype)
             q, k, v = (torch.from_numpy(x).to("cuda").to(dt) for x in host)
             idx = static if kind == "static" else rt.dynamic_index(q, k, keep, cfg.block)
             full, rho_t, r_t = rt.calibrate(q, k, v, idx)

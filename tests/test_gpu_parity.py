@@ -232,7 +232,7 @@ def _full_config(rt, n, nrows, all_rows):
     cfg = CONFIGS[n]
     log(f"config {n} ({cfg.name}): B={cfg.B} H={cfg.H} L={cfg.L} d={cfg.d} block={cfg.block} {cfg.dtype}")
     q, k, v = make_qkv(cfg.B, cfg.H, cfg.L, cfg.d, cfg.seed, scale=cfg.input_scale, dtype=cfg.dtype)
-    q2, k2, v2 = drift(q, k, v, n, 1, sigma=cfg.drift_sigma, scale=cfg.input_scale, dtype=cfg.dtype)
+    q2, k2, v2 = drift(q, k, v, n, 1, sigma=cfg.drift_sigma, dtype=cfg.dtype)
     rows = sample_rows(cfg.L, cfg.block, nrows, seed=n)
     rho_c, r_c = make_cache(cfg.B, cfg.H, cfg.L, cfg.d, seed=n, dtype=cfg.dtype)
     tq, tk, tv = (dev(x, cfg.dtype) for x in (q, k, v))
@@ -376,12 +376,13 @@ def test_slice_beyond_32bit_offsets(rt):
     assert_parity(host(rho_g[:, :, rows]), rho_o, "bf16", "calibrate rho")
     assert_parity(host(r_g[:, :, rows]), r_o, "bf16", "calibrate R")
     del tq, tk, tv
-    # the sparse step reads the GPU's own cache on the same strided layout
-    tq2, tk2, tv2 = (strided(x) for x in (q2, k2, v2))
-    o2_g = rt.sparse(tq2, tk2, tv2, idx, rho_g, r_g, lam=0.04, step=1)
+    # the sparse step on the same strided layout, both sides fed one seeded synthetic cache
+    del o_g, rho_g, r_g
+    rho_c, r_c = make_cache(B, H, L, d, seed=42)
+    tq2, tk2, tv2, tr = (strided(x) for x in (q2, k2, v2, r_c))
+    o2_g = rt.sparse(tq2, tk2, tv2, idx, torch.from_numpy(rho_c).cuda(), tr, lam=0.04, step=1)
     torch.cuda.synchronize()
-    rho_h, r_h = host(rho_g).astype(np.float64), host(r_g).astype(np.float64)
-    o2_o = oracle.sparse_step(q2, k2, v2, mask, block, rho_h[:, :, rows], r_h[:, :, rows], 0.04, 1, rows=rows)
+    o2_o = oracle.sparse_step(q2, k2, v2, mask, block, rho_c[:, :, rows], r_c[:, :, rows], 0.04, 1, rows=rows)
     assert_parity(host(o2_g[:, :, rows]), o2_o, "bf16", "sparse O'")
 
 
@@ -428,14 +429,15 @@ def test_refresh_period_replays_from_a_hip_graph(rt):
         torch.cuda.synchronize()
         for name, got, ref in zip(("O", "rho", "R", "O'1", "O'2", "O'3", "O'4"), (o_cal, rho, r_cal, *o_sp), want):
             assert torch.equal(got, ref), f"replay {replay}: {name} differs from the eager run"
-    # and the eager result itself against the oracle on the last sparse step
+    # and the eager period itself against the same period run by the oracle alone: its own
+    # calibration, its cache rounded to the I/O types, then sparse step 4
     mask = om.cogvideo3d_mask(nb, 2, 4)
-    _, rho_o, r_o = oracle.calibrate(*sets[0], mask, block)
-    rho_in = host(rho)
-    r_in = host(r_cal)
+    o_o, rho_o, r_o = oracle.calibrate(*sets[0], mask, block)
+    assert_parity(host(o_cal), o_o, "bf16", "calibrate O")
+    assert_parity(host(rho), rho_o, "bf16", "calibrate rho")
+    rho_in, r_in = rho_o.astype(np.float32), bf16_round(r_o.astype(np.float32))
     o4 = oracle.sparse_step(*sets[4], mask, block, rho_in, r_in, 0.04, 4)
-    assert_parity(host(o_sp[3]), o4, "bf16", "sparse O' (step 4)")
-    assert_parity(rho_in, rho_o, "bf16", "calibrate rho")
+    assert_parity(host(o_sp[3]), o4, "bf16", "sparse O' (step 4, period run by the library)")
 
 
 # ------------------------------------------------------------------ reads and stores stay inside the tensor
@@ -499,12 +501,14 @@ def test_tail_reads_and_stores_stay_inside_the_tensor(rt, case):
     assert_parity(host(inner(bo)), o_o, dtype, "calibrate O")
     assert_parity(host(rho), rho_o, dtype, "calibrate rho")
     assert_parity(host(inner(br)), r_o, dtype, "calibrate R")
-    # sparse step on drifted inputs, reading the GPU's own cache from the guarded R buffer
+    # sparse step on drifted inputs; both sides read the oracle's cache rounded to the I/O types,
+    # the library through a guarded R buffer
     q2, k2, v2 = drift(q, k, v, 91, 1, scale=scale, dtype=dtype)
     bq2, bk2, bv2 = (guarded_input(x) for x in (q2, k2, v2))
-    r_in = host(inner(br))
-    rho_in = host(rho)
-    br_in = guarded_input(r_in.astype(np.float32))
+    rho_in = rho_o.astype(np.float32)
+    r_in = bf16_round(r_o.astype(np.float32)) if dtype == "bf16" else r_o.astype(np.float32)
+    br_in = guarded_input(r_in)
+    rho.copy_(torch.from_numpy(rho_in).cuda())
     bo2 = guarded_output()
     rt.sparse(inner(bq2), inner(bk2), inner(bv2), idx, rho, inner(br_in), lam=0.04, step=2, out=inner(bo2))
     torch.cuda.synchronize()

@@ -55,7 +55,7 @@ class Config:
     masks: Tuple[MaskSpec, ...]
     sparse_steps: int     # sparse steps after each calibration
     input_scale: float = 1.0   # Q, K, V ~ N(0, input_scale^2)
-    drift_sigma: float = 0.05
+    drift_sigma: float = 0.05  # absolute step of the random walk: X + N(0, drift_sigma^2) per step
     lam: float = 0.04
 
     @property
