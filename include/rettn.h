@@ -229,6 +229,33 @@ rettn_status rettn_calibrate_residual(const rettn_desc* desc, const void* Q, con
                                       const rettn_index* idx, void* O, float* rho, void* R,
                                       rettn_residual kind, hipStream_t stream);
 
+/* rettn_calibrate_residual with a device workspace (the same step, Re-ttention
+ * summary page, "Approach"; review thread, replies to W1 of the first and
+ * second reviews).  For bfloat16 calibrations with 64- or 128-token blocks, V
+ * is first converted to float16 into the workspace, in V's own layout, by one
+ * pass over V; the attention kernel then streams the float16 tiles instead of
+ * re-encoding every V tile in every work-group.  The conversion is the one the
+ * kernel applies otherwise, so O, rho and R are bit for bit those of
+ * rettn_calibrate_residual.
+ *
+ * rettn_calibrate_workspace_bytes: the workspace the call needs for `desc`:
+ * ((B-1) stride_b + (H-1) stride_h + (L-1) stride_l + d) * 2 bytes (V's extent
+ * in float16) when the call takes that path, 0 otherwise (float32, 32-token
+ * blocks, or a slice too large for 32-bit offsets); RETTN_EINVAL for a bad
+ * descriptor, RETTN_EUNSUPPORTED for an extent beyond 2^50 elements.
+ *
+ * rettn_calibrate_ws: as rettn_calibrate_residual.  When the size above is
+ * not 0 the workspace must be 16-byte aligned, at least that size and overlap
+ * none of Q, K, V, O and R (each taken over the same extent), else
+ * RETTN_EINVAL with nothing launched; when it is 0 the workspace is ignored
+ * (it may be null).  The caller owns the workspace; its contents before and
+ * after the call mean nothing.  Two launches on `stream`, no allocation and
+ * no host wait, so the call can be captured in a HIP graph. */
+rettn_status rettn_calibrate_workspace_bytes(const rettn_desc* desc, size_t* bytes);
+rettn_status rettn_calibrate_ws(const rettn_desc* desc, const void* Q, const void* K, const void* V,
+                                const rettn_index* idx, void* workspace, size_t workspace_bytes,
+                                void* O, float* rho, void* R, rettn_residual kind, hipStream_t stream);
+
 /* Sparse step `step` (>= 1 sparse steps since the last calibration):
  *   O'_i = min(1, rho_i (1 + lambda step)) * softmax_{W(i)}(s') V'_{W(i)} + R_i
  * over the kept key blocks only (review thread, replies to W1 of the first

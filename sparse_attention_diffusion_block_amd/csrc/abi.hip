@@ -104,8 +104,27 @@ rettn_status rettn_calibrate_residual(const rettn_desc* desc, const void* Q, con
     AttnArgs a{};
     const rettn_status st = host::prepare_calibrate(desc, Q, K, V, idx, O, rho, R, kind, &a);
     if (st != RETTN_OK) return st;
-    const hipError_t e = desc->dtype == RETTN_BF16 ? rettn::launch_calibrate_bf16(a, desc->block, stream)
+    const hipError_t e = desc->dtype == RETTN_BF16 ? rettn::launch_calibrate_bf16(a, desc->block, nullptr, stream)
                                                    : rettn::launch_calibrate_f32(a, desc->block, stream);
+    return e == hipSuccess ? RETTN_OK : RETTN_EHIP;
+}
+
+rettn_status rettn_calibrate_workspace_bytes(const rettn_desc* desc, size_t* bytes) {
+    return host::calibrate_workspace(desc, bytes);
+}
+
+rettn_status rettn_calibrate_ws(const rettn_desc* desc, const void* Q, const void* K, const void* V,
+                                const rettn_index* idx, void* workspace, size_t workspace_bytes, void* O, float* rho,
+                                void* R, rettn_residual kind, hipStream_t stream) {
+    AttnArgs a{};
+    rettn_status st = host::prepare_calibrate(desc, Q, K, V, idx, O, rho, R, kind, &a);
+    if (st != RETTN_OK) return st;
+    size_t need = 0;
+    st = host::check_calibrate_workspace(desc, workspace, workspace_bytes, {Q, K, V, O, R}, &need);
+    if (st != RETTN_OK) return st;
+    const hipError_t e = desc->dtype == RETTN_BF16
+                             ? rettn::launch_calibrate_bf16(a, desc->block, need ? workspace : nullptr, stream)
+                             : rettn::launch_calibrate_f32(a, desc->block, stream);
     return e == hipSuccess ? RETTN_OK : RETTN_EHIP;
 }
 

@@ -48,4 +48,10 @@ inline bool slice_offsets_fit(const AttnArgs& a) {
     return rows * a.sl * 2 <= ((int64_t)1 << 31) - 256;
 }
 
+// The calibration kernel for 64- and 128-token blocks (bfloat16, d <= 128) takes a slice when its
+// 32-bit offsets fit; other calibrations run on the general kernels.
+inline bool calib_fast_path(const AttnArgs& a, int block) {
+    return (block == 64 || block == 128) && a.d <= 128 && slice_offsets_fit(a);
+}
+
 }  // namespace rettn

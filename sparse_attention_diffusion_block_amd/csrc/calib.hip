@@ -64,7 +64,7 @@ struct CalCfg {
     static constexpr int QSLOT = QLDS ? QT * RS : 8;
 };
 
-template <int BLOCK, int DP>
+template <int BLOCK, int DP, bool V16>
 __global__ void __launch_bounds__(CalCfg<DP>::NT, CalCfg<DP>::WPS) calib_kernel(const AttnArgs a) {
     using C = CalCfg<DP>;
     // [buffer][K | V][64 keys][RS]
@@ -109,10 +109,12 @@ __global__ void __launch_bounds__(CalCfg<DP>::NT, CalCfg<DP>::WPS) calib_kernel(
     }
 
     // Tile staging.  K: direct-to-LDS, wave w fills 1 KiB pieces w, w + NW, ...; lane -> (row, physical chunk).
-    // V: thread t holds 16-byte chunks t, t + NT, ... in registers until they are re-encoded and stored.
-    // (plain expressions only inside these lambdas: see the note in sparse64.hip)
+    // V, bfloat16: thread t holds 16-byte chunks t, t + NT, ... in registers until they are re-encoded and
+    // stored.  V16 (V already converted to float16 by v16_kernel): direct-to-LDS like K.
+    // (plain expressions only inside these lambdas: see the note in sparse64.hip; a buffer-load
+    // argument taken straight from an array element also suppressed the stub, hence the locals)
     const int nkt = (a.L + 63) / 64;
-    u32x4 vreg[C::VC];
+    u32x4 vreg[V16 ? 1 : C::VC];
     // A lane's byte offset within a tile is the same for every tile (a padded chunk takes an offset
     // past every record); the tile's row offset kt * 64 * row_bytes rides in the scalar offset.
     // (Each offset array is declared right before the lambda that reads it: other placements
@@ -135,25 +137,40 @@ __global__ void __launch_bounds__(CalCfg<DP>::NT, CalCfg<DP>::WPS) calib_kernel(
                 (uint32_t)kt * 64u * row_bytes, 0, 0);
         }
     };
-    uint32_t v_off[C::VC];
+    uint32_t v_off[V16 ? 1 : C::VC];
 #pragma unroll
-    for (int j = 0; j < C::VC; ++j) {
+    for (int j = 0; j < (V16 ? 0 : C::VC); ++j) {
         const int id = tid + j * C::NT;
         const int r = id / C::CPR;
         const int c = (id % C::CPR) ^ swz(r);
         v_off[j] = c * 8 < a.d ? (uint32_t)r * row_bytes + 16u * c : kOOB;
     }
-    auto issue_v = [&](int kt) {
+    // V tile kt towards slot buf (bfloat16: into registers now, into the slot at store_v)
+    auto issue_v = [&](int kt, int buf) {
+        if constexpr (V16) {
 #pragma unroll
-        for (int j = 0; j < C::VC; ++j) {
-            vreg[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, v_off[j], (uint32_t)kt * 64u * row_bytes, 0));
+            for (int j = 0; j < C::KL; ++j) {
+                const int piece = wave + j * C::NW;
+                const uint32_t off = k_off[j];
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rv, (__attribute__((address_space(3))) void*)(lds + buf * 2 * C::TILE + C::TILE + piece * 512), 16,
+                    off, (uint32_t)kt * 64u * row_bytes, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < C::VC; ++j) {
+                const uint32_t off = v_off[j];
+                vreg[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, (uint32_t)kt * 64u * row_bytes, 0));
+            }
         }
     };
     auto store_v = [&](int buf) {
+        if constexpr (!V16) {
 #pragma unroll
-        for (int j = 0; j < C::VC; ++j) {
-            const int id = tid + j * C::NT;
-            *(u32x4*)(lds + buf * 2 * C::TILE + C::TILE + id * 8) = bf16x8_to_f16x8(vreg[j]);
+            for (int j = 0; j < C::VC; ++j) {
+                const int id = tid + j * C::NT;
+                *(u32x4*)(lds + buf * 2 * C::TILE + C::TILE + id * 8) = bf16x8_to_f16x8(vreg[j]);
+            }
         }
     };
 
@@ -168,7 +185,7 @@ __global__ void __launch_bounds__(CalCfg<DP>::NT, CalCfg<DP>::WPS) calib_kernel(
     const int vrow = (4 * h + (s16 >> 2)) * C::RS;
 
     issue_k(0, 0);
-    issue_v(0);
+    issue_v(0, 0);
     store_v(0);
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __syncthreads();
@@ -178,7 +195,7 @@ __global__ void __launch_bounds__(CalCfg<DP>::NT, CalCfg<DP>::WPS) calib_kernel(
         const bool more = kt64 + 1 < nkt;
         if (more) {
             issue_k(kt64 + 1, buf ^ 1);
-            issue_v(kt64 + 1);
+            issue_v(kt64 + 1, buf ^ 1);
         }
         const uint16_t* ks = lds + buf * 2 * C::TILE;
         const uint16_t* vs = ks + C::TILE;
@@ -313,26 +330,47 @@ __global__ void __launch_bounds__(CalCfg<DP>::NT, CalCfg<DP>::WPS) calib_kernel(
         }
 }
 
-template <int BLOCK, int DP>
+// V converted once to float16 in V's own layout (exactly as the kernel's per-tile re-encoding would):
+// every (batch, head, row)'s d elements, 16 bytes per thread and step.
+__global__ void __launch_bounds__(256) v16_kernel(const AttnArgs a, uint16_t* __restrict__ out) {
+    const int64_t cpr = a.d / 8;                          // 16-byte chunks per row
+    const int64_t total = (int64_t)a.B * a.H * a.L * cpr;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t c = i % cpr, rowid = i / cpr;
+        const int64_t r = rowid % a.L, bh = rowid / a.L;
+        const int64_t b = bh / a.H, hd = bh - b * a.H;
+        const int64_t off = b * a.sb + hd * a.sh + r * a.sl + 8 * c;
+        const u32x4 w = *(const u32x4*)((const uint16_t*)a.V + off);
+        *(u32x4*)(out + off) = bf16x8_to_f16x8(w);
+    }
+}
+
+template <int BLOCK, int DP, bool V16>
 static hipError_t launch(AttnArgs a, hipStream_t s) {
     using C = CalCfg<DP>;
     const int64_t ntile = (a.L + C::QT - 1) / C::QT;
     const int64_t G = (int64_t)a.B * a.H * ntile;
     if (G <= 0 || G > 0x7fffffff) return hipErrorInvalidValue;
     a.G = (int32_t)G;
-    hipLaunchKernelGGL((calib_kernel<BLOCK, DP>), dim3((unsigned)G), dim3(C::NT), 0, s, a);
+    hipLaunchKernelGGL((calib_kernel<BLOCK, DP, V16>), dim3((unsigned)G), dim3(C::NT), 0, s, a);
     return hipGetLastError();
 }
 
 bool calib_supported(const AttnArgs& a, int block) {
     // every d up to 128: two accumulator sets fit at 2 waves per SIMD (Q in LDS at d = 128)
-    return (block == 64 || block == 128) && a.d <= 128 && slice_offsets_fit(a);
+    return calib_fast_path(a, block);
 }
 
-hipError_t launch_calib(AttnArgs a, int block, hipStream_t s) {
+hipError_t launch_calib(AttnArgs a, int block, void* v16, hipStream_t s) {
     const int dp = pad_d(a.d);
-#define RETTN_CASE(BL, D) \
-    if (block == BL && dp == D) return launch<BL, D>(a, s);
+    if (v16) {
+        hipLaunchKernelGGL(v16_kernel, dim3(2048), dim3(256), 0, s, a, (uint16_t*)v16);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        a.V = v16;
+    }
+#define RETTN_CASE(BL, D)                                                                  \
+    if (block == BL && dp == D) return v16 ? launch<BL, D, true>(a, s) : launch<BL, D, false>(a, s);
     RETTN_CASE(64, 32) RETTN_CASE(64, 64) RETTN_CASE(64, 96) RETTN_CASE(64, 128)
     RETTN_CASE(128, 32) RETTN_CASE(128, 64) RETTN_CASE(128, 96) RETTN_CASE(128, 128)
 #undef RETTN_CASE

@@ -102,6 +102,46 @@ rettn_status prepare_calibrate(const rettn_desc* desc, const void* Q, const void
     return RETTN_OK;
 }
 
+rettn_status calibrate_workspace(const rettn_desc* desc, size_t* bytes) {
+    if (!desc || !bytes) return RETTN_EINVAL;
+    const int64_t nb = desc->block > 0 ? cdiv(desc->L, desc->block) : 0;
+    rettn_index idx{};
+    idx.nqb = idx.nkb = (int32_t)nb;
+    rettn_status st = check_desc(desc, &idx);
+    if (st != RETTN_OK) return st;
+    *bytes = 0;
+    if (desc->dtype != RETTN_BF16) return RETTN_OK;
+    AttnArgs a{};
+    a.L = desc->L;
+    a.d = desc->d;
+    a.sl = desc->stride_l;
+    if (!calib_fast_path(a, desc->block)) return RETTN_OK;
+    // V's extent in elements: the last (batch, head, row)'s d elements end there.  The strides are
+    // unbounded int64 values, so the sum is formed in 128 bits and must stay below 2^50.
+    const __int128 last = (__int128)(desc->B - 1) * desc->stride_b + (__int128)(desc->H - 1) * desc->stride_h +
+                          (__int128)(desc->L - 1) * desc->stride_l + desc->d;
+    if (last > ((__int128)1 << 50)) return RETTN_EUNSUPPORTED;
+    *bytes = (size_t)last * 2u;
+    return RETTN_OK;
+}
+
+rettn_status check_calibrate_workspace(const rettn_desc* desc, const void* workspace, size_t workspace_bytes,
+                                       std::initializer_list<const void*> tensors, size_t* need) {
+    if (!need) return RETTN_EINVAL;
+    const rettn_status st = calibrate_workspace(desc, need);
+    if (st != RETTN_OK) return st;
+    if (*need == 0) return RETTN_OK;
+    if (!tensor_ok(workspace) || workspace_bytes < *need) return RETTN_EINVAL;
+    // every tensor spans the same extent in elements as V; the workspace must not touch any of them
+    const size_t esize = desc->dtype == RETTN_BF16 ? 2 : 4;
+    const uintptr_t w0 = (uintptr_t)workspace, w1 = w0 + *need;
+    for (const void* t : tensors) {
+        const uintptr_t t0 = (uintptr_t)t, t1 = t0 + *need / 2 * esize;
+        if (w0 < t1 && t0 < w1) return RETTN_EINVAL;
+    }
+    return RETTN_OK;
+}
+
 rettn_status prepare_sparse(const rettn_desc* desc, const void* Q, const void* K, const void* V,
                             const rettn_index* idx, const float* rho, const void* R, float lambda, int32_t step,
                             void* O, AttnArgs* args) {

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "../../include/rettn.h"
 #include "args.h"
 
@@ -18,6 +20,17 @@ int64_t cdiv(int64_t a, int64_t b);
 rettn_status prepare_calibrate(const rettn_desc* desc, const void* Q, const void* K, const void* V,
                                const rettn_index* idx, void* O, float* rho, void* R, rettn_residual kind,
                                AttnArgs* args);
+
+// Workspace of rettn_calibrate_ws for `desc`: the float16 copy of V in V's own layout when the
+// calibration kernel for 64/128-token blocks takes the call (bfloat16), else 0.  RETTN_EINVAL for a
+// bad descriptor.
+rettn_status calibrate_workspace(const rettn_desc* desc, size_t* bytes);
+
+// Checks of rettn_calibrate_ws's workspace (after prepare_calibrate): when the call needs one, it
+// must be 16-byte aligned, at least *need bytes and overlap none of the tensors (each spans the
+// descriptor's extent); *need is set to the size.  A workspace the call does not need is ignored.
+rettn_status check_calibrate_workspace(const rettn_desc* desc, const void* workspace, size_t workspace_bytes,
+                                       std::initializer_list<const void*> tensors, size_t* need);
 
 // Checks of rettn_sparse; on RETTN_OK, *args holds the kernel arguments (ramp = 1 + lambda step).
 rettn_status prepare_sparse(const rettn_desc* desc, const void* Q, const void* K, const void* V,

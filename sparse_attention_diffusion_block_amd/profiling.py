@@ -26,6 +26,7 @@ CSRC = os.path.join(HERE, "csrc")
 KERNEL_SOURCES = {
     "sparse64_kernel": ["sparse64.hip", "common.h", "attn.h", "args.h"],
     "calib_kernel": ["calib.hip", "common.h", "attn.h", "args.h"],
+    "v16_kernel": ["calib.hip", "common.h", "attn.h", "args.h"],
     "attn_bf16_kernel": ["attn_bf16.hip", "common.h", "attn.h", "args.h"],
     "attn_f32_kernel": ["attn_f32.hip", "common.h", "attn.h", "args.h"],
     "sparse_wg_kernel": ["sparse_wg.hip", "common.h", "attn.h", "args.h"],
@@ -50,7 +51,9 @@ def dispatched_kernels(dtype, block, d, L, stride_l=None):
     dp = _pad_d(d)
     if dtype == "f32":
         return f"attn_f32_kernel<{block}, {dp}, true>", f"attn_f32_kernel<{block}, {dp}, false>"
-    cal = f"calib_kernel<{block}, {dp}>" if block in (64, 128) and fits else f"attn_bf16_kernel<{block}, {dp}, true>"
+    # the binding's calibrate passes a workspace, so V is streamed in float16 (the third argument)
+    cal = (f"calib_kernel<{block}, {dp}, true>" if block in (64, 128) and fits
+           else f"attn_bf16_kernel<{block}, {dp}, true>")
     if block == 64 and d <= 64 and fits:
         sp = f"sparse64_kernel<{dp}>"
     elif (block == 128 or (block == 64 and d > 64)) and fits:

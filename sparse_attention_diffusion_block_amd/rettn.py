@@ -17,7 +17,7 @@ MASK_DIAG, MASK_BAND, MASK_COGVIDEO3D, MASK_FULL = 0, 1, 2, 3
 RESIDUAL_MASKED, RESIDUAL_DIFFERENCE = 0, 1
 EXPORTED = ("rettn_mask_build", "rettn_index_build", "rettn_index_build_sliced", "rettn_dynamic_workspace_bytes",
             "rettn_dynamic_index", "rettn_dynamic_index_noalloc", "rettn_calibrate", "rettn_calibrate_residual",
-            "rettn_sparse", "rettn_status_str")
+            "rettn_calibrate_workspace_bytes", "rettn_calibrate_ws", "rettn_sparse", "rettn_status_str")
 STATUS_ESCRATCH = 4
 NOALLOC_SCRATCH_BYTES = 32 << 20   # RETTN_NOALLOC_SCRATCH_BYTES
 
@@ -79,6 +79,11 @@ def lib():
         L.rettn_calibrate_residual.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, ctypes.POINTER(Index), vp, vp, vp,
                                                ctypes.c_int, vp]
         L.rettn_calibrate_residual.restype = ctypes.c_int
+        L.rettn_calibrate_workspace_bytes.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_size_t)]
+        L.rettn_calibrate_workspace_bytes.restype = ctypes.c_int
+        L.rettn_calibrate_ws.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, ctypes.POINTER(Index), vp, ctypes.c_size_t,
+                                         vp, vp, vp, ctypes.c_int, vp]
+        L.rettn_calibrate_ws.restype = ctypes.c_int
         L.rettn_sparse.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, ctypes.POINTER(Index), vp, vp,
                                    ctypes.c_float, i32, vp, vp]
         L.rettn_sparse.restype = ctypes.c_int
@@ -251,11 +256,24 @@ def _desc(t, block):
     return Desc(B, H, L, d, block, _dtype_code(t), sb, sh, sl)
 
 
-def calibrate(q, k, v, index, out=None, residual="masked"):
+def calibrate_workspace_bytes(q, block):
+    """Device workspace (bytes) rettn_calibrate_ws needs for tensors shaped and strided like q (0: none)."""
+    desc = _desc(q, block)
+    n = ctypes.c_size_t(0)
+    _check(lib().rettn_calibrate_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)),
+           "rettn_calibrate_workspace_bytes")
+    return int(n.value)
+
+
+def calibrate(q, k, v, index, out=None, residual="masked", workspace=None):
     """Full-attention calibration step -> (O, rho, R).  O and R have q's dtype; rho is float32 [B,H,L].
 
     residual="masked" gives Re-ttention's R (the masked keys' share of O); "difference" gives
-    the DiTFastAttn comparator's residual (full minus window attention)."""
+    the DiTFastAttn comparator's residual (full minus window attention).
+
+    workspace: None allocates the device workspace rettn_calibrate_ws needs (V in float16); a
+    uint8 tensor of at least calibrate_workspace_bytes(q, block) bytes on q's device is used as
+    given; False calls rettn_calibrate_residual, which takes no workspace (same results)."""
     import torch
     q, k, v = _prep((q, k, v))
     B, H, L, d = q.shape
@@ -271,9 +289,23 @@ def calibrate(q, k, v, index, out=None, residual="masked"):
     desc = _desc(q, index.block)
     idx = index.c_struct()
     kind = {"masked": RESIDUAL_MASKED, "difference": RESIDUAL_DIFFERENCE}[residual]
-    _check(lib().rettn_calibrate_residual(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                          ctypes.byref(idx), o.data_ptr(), rho.data_ptr(), r.data_ptr(), kind,
-                                          _stream(q.device)), "rettn_calibrate_residual")
+    if workspace is False:
+        _check(lib().rettn_calibrate_residual(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                              ctypes.byref(idx), o.data_ptr(), rho.data_ptr(), r.data_ptr(), kind,
+                                              _stream(q.device)), "rettn_calibrate_residual")
+        return o, rho, r
+    need = calibrate_workspace_bytes(q, index.block)
+    ws_ptr, ws_bytes = None, 0
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        elif (not workspace.is_cuda or workspace.device != q.device or workspace.dtype != torch.uint8
+              or not workspace.is_contiguous() or workspace.numel() < need):
+            raise ValueError(f"workspace must be a contiguous uint8 tensor of at least {need} bytes on Q's device")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    _check(lib().rettn_calibrate_ws(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(idx),
+                                    ws_ptr, ws_bytes, o.data_ptr(), rho.data_ptr(), r.data_ptr(), kind,
+                                    _stream(q.device)), "rettn_calibrate_ws")
     return o, rho, r
 
 

@@ -102,6 +102,48 @@ static void check_workspace() {
 // A fake device address: aligned or not, never dereferenced by the checks.
 static void* addr(uintptr_t a) { return (void*)a; }
 
+// The calibration workspace: V's extent in float16 on the 64/128-token-block path, 0 elsewhere,
+// computed without overflow for any stride; its checks refuse null, misaligned, short and
+// overlapping workspaces.
+static void check_calib_workspace() {
+    rettn_desc d = good_desc();
+    size_t n = 1;
+    EXPECT(host::calibrate_workspace(&d, &n) == RETTN_OK && n == (size_t)2 * 3 * 200 * 64 * 2);
+    EXPECT(host::calibrate_workspace(nullptr, &n) == RETTN_EINVAL);
+    EXPECT(host::calibrate_workspace(&d, nullptr) == RETTN_EINVAL);
+    rettn_desc f = good_desc();
+    f.dtype = RETTN_F32;
+    EXPECT(host::calibrate_workspace(&f, &n) == RETTN_OK && n == 0);
+    f = good_desc();
+    f.block = 32;
+    EXPECT(host::calibrate_workspace(&f, &n) == RETTN_OK && n == 0);
+    for (int64_t big : {(int64_t)1 << 40, (int64_t)1 << 55, INT64_MAX - 7}) {
+        rettn_desc e = good_desc();
+        e.stride_b = big & ~(int64_t)7;
+        const rettn_status st = host::calibrate_workspace(&e, &n);
+        EXPECT(st == RETTN_OK || st == RETTN_EUNSUPPORTED);
+        if (st == RETTN_OK) EXPECT(n == (size_t)((e.stride_b + 2 * e.stride_h + 199 * e.stride_l + 64) * 2));
+    }
+    const size_t need = (size_t)2 * 3 * 200 * 64 * 2;
+    const uintptr_t base = (uintptr_t)1 << 40, gap = (uintptr_t)1 << 30;
+    const void* t5[5] = {addr(base), addr(base + gap), addr(base + 2 * gap), addr(base + 3 * gap), addr(base + 4 * gap)};
+    auto check = [&](uintptr_t ws, size_t bytes) {
+        size_t nd = 0;
+        return host::check_calibrate_workspace(&d, addr(ws), bytes, {t5[0], t5[1], t5[2], t5[3], t5[4]}, &nd);
+    };
+    EXPECT(check(base + 8 * gap, need) == RETTN_OK);
+    EXPECT(check(base + 8 * gap, need - 1) == RETTN_EINVAL);
+    EXPECT(check(base + 8 * gap + 4, need) == RETTN_EINVAL);
+    EXPECT(check(0, need) == RETTN_EINVAL);
+    EXPECT(check(base + 2 * gap, need) == RETTN_EINVAL);                 // V itself
+    EXPECT(check(base + gap - need + 16, need) == RETTN_EINVAL);         // ends inside the second tensor
+    EXPECT(check(base + 3 * gap + need - 16, need) == RETTN_EINVAL);     // starts inside the fourth
+    EXPECT(check(base + gap - need, need) == RETTN_OK);                  // just before the second
+    size_t nd = 7;
+    EXPECT(host::check_calibrate_workspace(&f, nullptr, 0, {t5[0]}, &nd) == RETTN_OK && nd == 0);
+    EXPECT(host::check_calibrate_workspace(&d, addr(base + 8 * gap), need, {t5[0]}, nullptr) == RETTN_EINVAL);
+}
+
 static void check_attention_args() {
     const uintptr_t A = 0x100000;              // 16-byte aligned
     int32_t rp[8], ci[8];
@@ -225,6 +267,7 @@ int main() {
     check_masks();
     check_status_strings();
     check_workspace();
+    check_calib_workspace();
     check_attention_args();
     check_dynamic_and_index_build();
     printf("host checks passed: %d expectations\n", g_checks);

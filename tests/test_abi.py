@@ -177,6 +177,68 @@ def test_dynamic_workspace_size():
     assert lib.rettn_dynamic_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == EINVAL
 
 
+def _calib_ws_bytes(d):
+    n = ctypes.c_size_t(12345)
+    st = rt.lib().rettn_calibrate_workspace_bytes(ctypes.byref(d), ctypes.byref(n))
+    return st, n.value
+
+
+def test_calibrate_workspace_size():
+    """V's extent in float16 when the 64/128-token-block kernel takes the call, else 0."""
+    d = _good_desc()                     # B 2, H 3, L 200, d 64, contiguous
+    assert _calib_ws_bytes(d) == (0, 2 * 3 * 200 * 64 * 2)
+    d.block = 128
+    assert _calib_ws_bytes(d) == (0, 2 * 3 * 200 * 64 * 2)
+    d.block = 32                         # the general kernels: no conversion pass
+    assert _calib_ws_bytes(d) == (0, 0)
+    d = _good_desc()
+    d.dtype = b.RETTN_F32
+    assert _calib_ws_bytes(d) == (0, 0)
+    # strided layouts: the extent up to the last row's d elements, in V's own layout
+    d = b.Desc(2, 3, 200, 64, 64, b.RETTN_BF16, 5 * 256 * 96, 256 * 96, 96)      # padded rows and slices
+    assert _calib_ws_bytes(d) == (0, (1 * 5 * 256 * 96 + 2 * 256 * 96 + 199 * 96 + 64) * 2)
+    d = b.Desc(2, 3, 200, 64, 64, b.RETTN_BF16, 200 * 3 * 64, 64, 3 * 64)         # [B, L, H, d] order
+    assert _calib_ws_bytes(d) == (0, (200 * 3 * 64 + 2 * 64 + 199 * 3 * 64 + 64) * 2)
+    # a slice past 32-bit offsets takes the general kernel: no workspace
+    d = b.Desc(1, 1, 1 << 17, 64, 64, b.RETTN_BF16, (1 << 17) * 8192, (1 << 17) * 8192, 8192)
+    assert _calib_ws_bytes(d) == (0, 0)
+    # an extent beyond 2^50 elements, a bad descriptor, a null output
+    d = b.Desc(2, 1, 200, 64, 64, b.RETTN_BF16, 1 << 60, 200 * 64, 64)
+    assert _calib_ws_bytes(d)[0] == 2                 # RETTN_EUNSUPPORTED
+    d = _good_desc()
+    d.d = 0
+    assert _calib_ws_bytes(d)[0] == EINVAL
+    assert rt.lib().rettn_calibrate_workspace_bytes(ctypes.byref(_good_desc()), None) == EINVAL
+
+
+def test_calibrate_ws_rejects_bad_workspaces():
+    """Nothing is launched for a workspace that is null, misaligned, too small or overlaps a tensor."""
+    lib = rt.lib()
+    d = _good_desc()
+    need = 2 * 3 * 200 * 64 * 2
+    idx = _idx()
+    base = 1 << 40                       # tensors far apart, 16-byte aligned; never dereferenced
+    q, k, v, o, r, rho = (base + i * (1 << 30) for i in range(6))
+    ws_ok = base + 8 * (1 << 30)
+
+    def call(ws=ws_ok, ws_bytes=need, kind=b.RESIDUAL_MASKED, desc=d, **tensors):
+        t = dict(q=q, k=k, v=v, o=o, r=r)
+        t.update(tensors)
+        return lib.rettn_calibrate_ws(ctypes.byref(desc), t["q"], t["k"], t["v"], ctypes.byref(idx), ws, ws_bytes,
+                                      t["o"], rho, t["r"], kind, None)
+    assert call(ws=None) == EINVAL
+    assert call(ws=ws_ok + 8) == EINVAL
+    assert call(ws_bytes=need - 1) == EINVAL
+    assert call(ws=v) == EINVAL                       # the workspace is V itself
+    assert call(ws=o + need - 16) == EINVAL           # its first bytes overlap O's last ones
+    assert call(ws=q - need + 16) == EINVAL           # its last bytes overlap Q's first ones
+    assert call(kind=7) == EINVAL
+    bad = _good_desc()
+    bad.d = 0
+    assert call(desc=bad) == EINVAL
+    assert call(q=FAKE + 8) == EINVAL
+
+
 def test_dynamic_index_rejects_bad_arguments():
     lib = rt.lib()
     d = _good_desc()

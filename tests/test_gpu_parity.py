@@ -221,6 +221,83 @@ def test_bitwise_deterministic(rt, d):
                            b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
 
 
+# ------------------------------------------------------------------ the workspace path of the calibration
+WS_CASES = [
+    # name, B, H, L, d, block, row pitch (None: contiguous), layout, mask maker
+    ("d64-b64-cog-tail", 2, 3, 1000, 64, 64, None, "bhld", lambda nb: om.cogvideo3d_mask(nb, 2, 4)),
+    ("d72-b64-band-pitch80", 2, 2, 333, 72, 64, 80, "bhld", lambda nb: om.band_mask(nb, 2)),
+    ("d88-b64-blhd", 2, 3, 300, 88, 64, None, "blhd", lambda nb: random_mask(nb, nb, 0.4, 21, empty_rows=(1,))),
+    ("d128-b128-band-tail", 1, 2, 390, 128, 128, None, "bhld", lambda nb: om.band_mask(nb, 1)),
+    ("d32-b64-full", 1, 2, 200, 32, 64, None, "bhld", lambda nb: om.full_mask(nb)),
+    ("d96-b128-tail", 2, 1, 300, 96, 128, 104, "bhld", lambda nb: om.band_mask(nb, 2)),
+]
+
+
+@pytest.mark.parametrize("case", WS_CASES, ids=[c[0] for c in WS_CASES])
+def test_calibrate_workspace_path_is_bit_identical(rt, case):
+    """rettn_calibrate_ws (V converted to float16 once into the workspace, then streamed) gives the
+    bits of rettn_calibrate_residual (V re-encoded per tile) for both residual kinds, in strided and
+    head-interleaved layouts; a caller-supplied, larger workspace reused by a second call works too.
+    Both are also checked against the oracle."""
+    import torch
+    name, B, H, L, d, block, pitch, layout, make_mask = case
+    log(f"case ws {name}: B={B} H={H} L={L} d={d} block={block} pitch={pitch} layout={layout}")
+    q, k, v = make_qkv(B, H, L, d, 31)
+    nb = -(-L // block)
+    mask = make_mask(nb)
+    idx = rt.index_build(mask, block)
+
+    def place(x):
+        t = torch.from_numpy(x).to(torch.bfloat16).cuda()
+        if layout == "blhd":
+            return t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+        if pitch is None:
+            return t
+        buf = torch.full((B, H, L, pitch), float("nan"), dtype=torch.bfloat16, device="cuda")
+        buf[..., :d] = t
+        return buf[..., :d]
+    tq, tk, tv = (place(x) for x in (q, k, v))
+    need = rt.calibrate_workspace_bytes(tq, block)
+    assert need > 0
+    ws = torch.empty(need + 4096, dtype=torch.uint8, device="cuda")
+    o_o, rho_o, r_o = oracle.calibrate(q, k, v, mask, block)
+    for residual in ("masked", "difference"):
+        ref = rt.calibrate(tq, tk, tv, idx, residual=residual, workspace=False)
+        got = rt.calibrate(tq, tk, tv, idx, residual=residual, workspace=ws)
+        auto = rt.calibrate(tq, tk, tv, idx, residual=residual)
+        torch.cuda.synchronize()
+        for what, a, b, c in zip(("O", "rho", "R"), ref, got, auto):
+            bits = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
+            assert torch.equal(a.contiguous().view(bits), b.contiguous().view(bits)), f"{residual} {what}: ws path"
+            assert torch.equal(a.contiguous().view(bits), c.contiguous().view(bits)), f"{residual} {what}: auto ws"
+        if residual == "masked":
+            assert_parity(host(got[0]), o_o, "bf16", "calibrate O")
+            assert_parity(host(got[1]), rho_o, "bf16", "calibrate rho")
+            assert_parity(host(got[2]), r_o, "bf16", "calibrate R")
+    # the same workspace, now for a smaller problem (its old contents mean nothing)
+    q2, k2, v2 = make_qkv(1, 1, 150, d, 32)
+    idx2 = rt.index_build(make_mask(-(-150 // block)), block)
+    a2 = [torch.from_numpy(x).to(torch.bfloat16).cuda() for x in (q2, k2, v2)]
+    ref2 = rt.calibrate(*a2, idx2, workspace=False)
+    got2 = rt.calibrate(*a2, idx2, workspace=ws)
+    torch.cuda.synchronize()
+    for a, b in zip(ref2, got2):
+        bits = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
+        assert torch.equal(a.view(bits), b.view(bits))
+
+
+def test_calibrate_binding_rejects_small_workspace(rt):
+    import torch
+    q, k, v = (torch.zeros(1, 1, 128, 64, dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    idx = rt.index_build(om.full_mask(2), 64)
+    need = rt.calibrate_workspace_bytes(q, 64)
+    assert need == 128 * 64 * 2
+    with pytest.raises(ValueError):
+        rt.calibrate(q, k, v, idx, workspace=torch.empty(need - 16, dtype=torch.uint8, device="cuda"))
+    with pytest.raises(ValueError):
+        rt.calibrate(q, k, v, idx, workspace=torch.empty(need // 4, dtype=torch.float32, device="cuda"))
+
+
 # ------------------------------------------------------------------ full-size workloads
 def _full_config(rt, n, nrows, all_rows):
     """Workload n at its full size, in the launch configuration the bench times.
