@@ -231,26 +231,38 @@ rettn_status rettn_calibrate_residual(const rettn_desc* desc, const void* Q, con
 
 /* rettn_calibrate_residual with a device workspace (the same step, Re-ttention
  * summary page, "Approach"; review thread, replies to W1 of the first and
- * second reviews).  For bfloat16 calibrations with 64- or 128-token blocks, V
- * is first converted to float16 into the workspace, in V's own layout, by one
- * pass over V; the attention kernel then streams the float16 tiles instead of
- * re-encoding every V tile in every work-group.  The conversion is the one the
- * kernel applies otherwise, so O, rho and R are bit for bit those of
- * rettn_calibrate_residual.
+ * second reviews).  For bfloat16 calibrations with 64- or 128-token blocks:
+ *   - V is first converted to float16 into the workspace, in V's own layout,
+ *     by one pass over V; the attention kernel then streams the float16 tiles
+ *     instead of re-encoding every V tile in every work-group.  The conversion
+ *     is the one the kernel applies otherwise;
+ *   - when the work-groups fill at least one round of the current device and
+ *     leave a last round at most half full, the last round's groups are cut
+ *     into parts along the key range (up to 8, at least two key tiles each);
+ *     each part leaves its partial softmax state (reference, both
+ *     denominators, both P*V sums) in the workspace and a second pass merges
+ *     them into O, rho and R.
+ * Without a split, O, rho and R are bit for bit those of
+ * rettn_calibrate_residual; the rows of split groups differ from them only by
+ * the order of float32 additions.
  *
- * rettn_calibrate_workspace_bytes: the workspace the call needs for `desc`:
- * ((B-1) stride_b + (H-1) stride_h + (L-1) stride_l + d) * 2 bytes (V's extent
- * in float16) when the call takes that path, 0 otherwise (float32, 32-token
- * blocks, or a slice too large for 32-bit offsets); RETTN_EINVAL for a bad
- * descriptor, RETTN_EUNSUPPORTED for an extent beyond 2^50 elements.
+ * rettn_calibrate_workspace_bytes: the workspace the call needs for `desc` on
+ * the current device: V's extent in float16,
+ * ((B-1) stride_b + (H-1) stride_h + (L-1) stride_l + d) * 2 bytes, rounded up
+ * to 256 and followed by parts * rows * (4 + 2 * dp) * 4 bytes of partial
+ * states when a split is planned (dp = d rounded up to 32, 64, 96 or 128;
+ * rows = 128 or 256 per group); 0 when the call takes neither (float32,
+ * 32-token blocks, or a slice too large for 32-bit offsets).  RETTN_EINVAL for
+ * a bad descriptor, RETTN_EUNSUPPORTED for an extent beyond 2^50 elements.
  *
- * rettn_calibrate_ws: as rettn_calibrate_residual.  When the size above is
- * not 0 the workspace must be 16-byte aligned, at least that size and overlap
- * none of Q, K, V, O and R (each taken over the same extent), else
- * RETTN_EINVAL with nothing launched; when it is 0 the workspace is ignored
- * (it may be null).  The caller owns the workspace; its contents before and
- * after the call mean nothing.  Two launches on `stream`, no allocation and
- * no host wait, so the call can be captured in a HIP graph. */
+ * rettn_calibrate_ws: as rettn_calibrate_residual, with the size queried while
+ * the same device is current.  When that size is not 0 the workspace must be
+ * 16-byte aligned, at least that size and overlap none of Q, K, V, O and R
+ * (each taken over V's extent), else RETTN_EINVAL with nothing launched; when
+ * it is 0 the workspace is ignored (it may be null).  The caller owns the
+ * workspace; its contents before and after the call mean nothing.  Two or
+ * three launches on `stream`, no allocation and no host wait, so the call can
+ * be captured in a HIP graph. */
 rettn_status rettn_calibrate_workspace_bytes(const rettn_desc* desc, size_t* bytes);
 rettn_status rettn_calibrate_ws(const rettn_desc* desc, const void* Q, const void* K, const void* V,
                                 const rettn_index* idx, void* workspace, size_t workspace_bytes,

@@ -35,6 +35,27 @@ void* scratch_for_current_device() {
     return g_scratch_ptr[dev];
 }
 
+// Layout of rettn_calibrate_ws's workspace: V in float16 over V's extent, then (256-byte aligned)
+// the partial states of a split last round, when one is planned on the current device.
+struct CalibWorkspace {
+    size_t v16 = 0, part_offset = 0, part = 0, total = 0;
+};
+
+rettn_status calib_workspace(const rettn_desc* desc, CalibWorkspace* w) {
+    rettn_status st = host::calibrate_workspace(desc, &w->v16);
+    if (st != RETTN_OK || w->v16 == 0) return st;
+    AttnArgs a{};
+    a.B = desc->B;
+    a.H = desc->H;
+    a.L = desc->L;
+    a.d = desc->d;
+    a.sl = desc->stride_l;
+    w->part_offset = (w->v16 + 255) / 256 * 256;
+    w->part = rettn::calib_split_bytes(a, desc->block);
+    w->total = w->part ? w->part_offset + w->part : w->v16;
+    return RETTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -104,13 +125,18 @@ rettn_status rettn_calibrate_residual(const rettn_desc* desc, const void* Q, con
     AttnArgs a{};
     const rettn_status st = host::prepare_calibrate(desc, Q, K, V, idx, O, rho, R, kind, &a);
     if (st != RETTN_OK) return st;
-    const hipError_t e = desc->dtype == RETTN_BF16 ? rettn::launch_calibrate_bf16(a, desc->block, nullptr, stream)
-                                                   : rettn::launch_calibrate_f32(a, desc->block, stream);
+    const hipError_t e = desc->dtype == RETTN_BF16
+                             ? rettn::launch_calibrate_bf16(a, desc->block, nullptr, nullptr, stream)
+                             : rettn::launch_calibrate_f32(a, desc->block, stream);
     return e == hipSuccess ? RETTN_OK : RETTN_EHIP;
 }
 
 rettn_status rettn_calibrate_workspace_bytes(const rettn_desc* desc, size_t* bytes) {
-    return host::calibrate_workspace(desc, bytes);
+    if (!bytes) return RETTN_EINVAL;
+    CalibWorkspace w;
+    const rettn_status st = calib_workspace(desc, &w);
+    if (st == RETTN_OK) *bytes = w.total;
+    return st;
 }
 
 rettn_status rettn_calibrate_ws(const rettn_desc* desc, const void* Q, const void* K, const void* V,
@@ -119,12 +145,15 @@ rettn_status rettn_calibrate_ws(const rettn_desc* desc, const void* Q, const voi
     AttnArgs a{};
     rettn_status st = host::prepare_calibrate(desc, Q, K, V, idx, O, rho, R, kind, &a);
     if (st != RETTN_OK) return st;
-    size_t need = 0;
-    st = host::check_calibrate_workspace(desc, workspace, workspace_bytes, {Q, K, V, O, R}, &need);
+    CalibWorkspace w;
+    st = calib_workspace(desc, &w);
     if (st != RETTN_OK) return st;
-    const hipError_t e = desc->dtype == RETTN_BF16
-                             ? rettn::launch_calibrate_bf16(a, desc->block, need ? workspace : nullptr, stream)
-                             : rettn::launch_calibrate_f32(a, desc->block, stream);
+    st = host::check_calibrate_workspace(workspace, workspace_bytes, w.total, w.v16, {Q, K, V, O, R});
+    if (st != RETTN_OK) return st;
+    void* v16 = w.total ? workspace : nullptr;
+    void* part = w.part ? (char*)workspace + w.part_offset : nullptr;
+    const hipError_t e = desc->dtype == RETTN_BF16 ? rettn::launch_calibrate_bf16(a, desc->block, v16, part, stream)
+                                                   : rettn::launch_calibrate_f32(a, desc->block, stream);
     return e == hipSuccess ? RETTN_OK : RETTN_EHIP;
 }
 

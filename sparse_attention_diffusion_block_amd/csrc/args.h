@@ -32,6 +32,13 @@ struct AttnArgs {
     // col_idx + slice * col_stride.
     int32_t slice_mod;
     int64_t col_stride;
+    // Calibration only (64/128-token-block kernel): the last, partial round of work-groups may be
+    // split along the key range.  Work items at or past split_from are (group, part) pairs: part p
+    // of nsplit walks key tiles [p * nkt / nsplit, (p + 1) * nkt / nsplit) and stores its partial
+    // softmax state in `part` (see calib.hip) instead of O, rho and R; a merge pass combines them.
+    int32_t split_from;       // first split group; no split when nsplit <= 1
+    int32_t nsplit;
+    float* part;
 };
 
 // d is padded to DP in {32, 64, 96, 128} inside the kernels.

@@ -9,8 +9,9 @@
 namespace rettn {
 
 // v16: null, or device memory covering V's extent that receives V in float16 first (bfloat16
-// calibrations on the 64/128-token-block kernel; ignored by the other paths).
-hipError_t launch_calibrate_bf16(AttnArgs a, int block, void* v16, hipStream_t s);
+// calibrations on the 64/128-token-block kernel; ignored by the other paths).  part: null, or
+// calib_split_bytes(a, block) bytes for the partial states of a split last round (with v16 only).
+hipError_t launch_calibrate_bf16(AttnArgs a, int block, void* v16, void* part, hipStream_t s);
 hipError_t launch_sparse_bf16(AttnArgs a, int block, hipStream_t s);
 hipError_t launch_calibrate_f32(AttnArgs a, int block, hipStream_t s);
 hipError_t launch_sparse_f32(AttnArgs a, int block, hipStream_t s);
@@ -25,9 +26,13 @@ bool sparse_wg_supported(const AttnArgs& a, int block);
 hipError_t launch_sparse_wg(AttnArgs a, int block, hipStream_t s);
 
 // Calibration for 64- and 128-token blocks (bfloat16): 128 or 256 query rows per work-group.  With
-// v16 set, V is first converted to float16 into v16 (same layout) and streamed from there.
+// v16 set, V is first converted to float16 into v16 (same layout) and streamed from there; with
+// part set too, a last round of work-groups at most half full is split along the key range and
+// merged by a second pass (calib_split_bytes: the partial states' size on the current device,
+// 0 when no split is planned).
 bool calib_supported(const AttnArgs& a, int block);
-hipError_t launch_calib(AttnArgs a, int block, void* v16, hipStream_t s);
+size_t calib_split_bytes(const AttnArgs& a, int block);
+hipError_t launch_calib(AttnArgs a, int block, void* v16, void* part, hipStream_t s);
 
 // CSR of `slices` masks [slices, nqb, nkb]; slice s's ids start at col_idx + s * nqb * nkb.
 hipError_t launch_index_build(const uint8_t* mask, int slices, int nqb, int nkb, int32_t* row_ptr, int32_t* col_idx,

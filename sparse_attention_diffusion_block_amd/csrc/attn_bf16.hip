@@ -348,8 +348,8 @@ static hipError_t dispatch(AttnArgs a, int block, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_calibrate_bf16(AttnArgs a, int block, void* v16, hipStream_t s) {
-    if (calib_supported(a, block)) return launch_calib(a, block, v16, s);
+hipError_t launch_calibrate_bf16(AttnArgs a, int block, void* v16, void* part, hipStream_t s) {
+    if (calib_supported(a, block)) return launch_calib(a, block, v16, part, s);
     return dispatch<true>(a, block, s);
 }
 hipError_t launch_sparse_bf16(AttnArgs a, int block, hipStream_t s) {

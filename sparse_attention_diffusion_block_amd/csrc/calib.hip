@@ -25,6 +25,8 @@
 //   * softmax against a running reference per row: a tile is redone against
 //     its true max only when a row's packed float16 sum is non-finite or
 //     above 2^14 (then all four accumulators are rescaled).
+#include <algorithm>
+
 #include "attn.h"
 #include "common.h"
 
@@ -77,9 +79,25 @@ __global__ void __launch_bounds__(CalCfg<DP>::NT, CalCfg<DP>::WPS) calib_kernel(
     const int h = lane >> 5, n = lane & 31;
 
     const int ntile = (a.L + C::QT - 1) / C::QT;
-    const int work = xcd_remap(blockIdx.x, a.G);
-    const int bh = work / ntile;
-    const int tile = work - bh * ntile;
+    const int nkt = (a.L + 63) / 64;
+    // Work-groups are dispatched in order, round-robin over the XCDs.  With a split last round the
+    // whole groups come first and the parts after them, each run spread evenly over the XCDs (so
+    // that every XCD gets its share of both), each XCD taking a contiguous range of either.
+    const int blk = blockIdx.x;
+    const int work = a.nsplit <= 1 ? xcd_remap(blk, a.G)
+                     : blk < a.split_from ? xcd_remap(blk, a.split_from)
+                                          : a.split_from + xcd_remap(blk - a.split_from, a.G - a.split_from);
+    // a work item of the split last round is part `part` of group `grp`, over key tiles [kt_lo, kt_hi)
+    int grp = work, part = -1, kt_lo = 0, kt_hi = nkt;
+    if (a.nsplit > 1 && work >= a.split_from) {
+        const int t = work - a.split_from;
+        grp = a.split_from + t / a.nsplit;
+        part = t - (t / a.nsplit) * a.nsplit;
+        kt_lo = (int)((int64_t)part * nkt / a.nsplit);
+        kt_hi = (int)((int64_t)(part + 1) * nkt / a.nsplit);
+    }
+    const int bh = grp / ntile;
+    const int tile = grp - bh * ntile;
     const int bi = bh / a.H, hi = bh - bi * a.H;
     const int64_t base = (int64_t)bi * a.sb + (int64_t)hi * a.sh;
     const int q0 = tile * C::QT + wave * 32;
@@ -113,7 +131,6 @@ __global__ void __launch_bounds__(CalCfg<DP>::NT, CalCfg<DP>::WPS) calib_kernel(
     // stored.  V16 (V already converted to float16 by v16_kernel): direct-to-LDS like K.
     // (plain expressions only inside these lambdas: see the note in sparse64.hip; a buffer-load
     // argument taken straight from an array element also suppressed the stub, hence the locals)
-    const int nkt = (a.L + 63) / 64;
     u32x4 vreg[V16 ? 1 : C::VC];
     // A lane's byte offset within a tile is the same for every tile (a padded chunk takes an offset
     // past every record); the tile's row offset kt * 64 * row_bytes rides in the scalar offset.
@@ -184,15 +201,15 @@ __global__ void __launch_bounds__(CalCfg<DP>::NT, CalCfg<DP>::WPS) calib_kernel(
     const int fv = ((s16 >> 2) << 1) | h;
     const int vrow = (4 * h + (s16 >> 2)) * C::RS;
 
-    issue_k(0, 0);
-    issue_v(0, 0);
+    issue_k(kt_lo, 0);
+    issue_v(kt_lo, 0);
     store_v(0);
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __syncthreads();
 
-    for (int kt64 = 0; kt64 < nkt; ++kt64) {
-        const int buf = kt64 & 1;
-        const bool more = kt64 + 1 < nkt;
+    for (int kt64 = kt_lo; kt64 < kt_hi; ++kt64) {
+        const int buf = (kt64 - kt_lo) & 1;
+        const bool more = kt64 + 1 < kt_hi;
         if (more) {
             issue_k(kt64 + 1, buf ^ 1);
             issue_v(kt64 + 1, buf ^ 1);
@@ -299,6 +316,30 @@ __global__ void __launch_bounds__(CalCfg<DP>::NT, CalCfg<DP>::WPS) calib_kernel(
 
     // Epilogue.  Lane (n, h) owns d = 32 dt + 8 bb + 4 h + r of row `row`.
     const float din = xhalf_sum(d_in), dout = xhalf_sum(d_out);
+    if (part >= 0) {
+        // partial state of this part, against its own reference mref (log2 units):
+        // {mref, D_in, D_out, 0}, then N_in[DP], then N_out[DP], per row of the split groups
+        if (!row_ok) return;
+        const int64_t tail_rows = (int64_t)(a.G - a.split_from) / a.nsplit * C::QT;
+        const int64_t trow = (int64_t)(grp - a.split_from) * C::QT + wave * 32 + n;
+        float* rec = a.part + ((int64_t)part * tail_rows + trow) * (4 + 2 * DP);
+        if (h == 0) *(f32x4*)rec = f32x4{mref, din, dout, 0.f};
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                const int d0 = 32 * dt + 8 * bb + 4 * h;
+                f32x4 vi, vo;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    vi[r] = acc_in[dt][4 * bb + r];
+                    vo[r] = acc_out[dt][4 * bb + r];
+                }
+                *(f32x4*)(rec + 4 + d0) = vi;
+                *(f32x4*)(rec + 4 + DP + d0) = vo;
+            }
+        return;
+    }
     const float inv = 1.f / (din + dout);
     // window attention's normaliser for the difference residual (no kept key: the window output is 0)
     const float inv_in = din > 0.f ? 1.f / din : 0.f;
@@ -345,14 +386,121 @@ __global__ void __launch_bounds__(256) v16_kernel(const AttnArgs a, uint16_t* __
     }
 }
 
+// Combines the nsplit partial states of every row of the split groups (written by the parts'
+// epilogue) into O, rho and R: the parts' sums are brought to the largest of their references and
+// added, then the calibration's own epilogue arithmetic follows.  One thread per 4 elements of a row.
+template <int DP>
+__global__ void __launch_bounds__(256) calib_merge_kernel(const AttnArgs a) {
+    using C = CalCfg<DP>;
+    constexpr int REC = 4 + 2 * DP;
+    const int ntile = (a.L + C::QT - 1) / C::QT;
+    const int64_t tail_rows = (int64_t)(a.G - a.split_from) / a.nsplit * C::QT;
+    const int cpr = a.d / 4;
+    const int64_t total = tail_rows * cpr;
+    const bool diff = a.residual != 0;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t trow = i / cpr;
+        const int c4 = (int)(i - trow * cpr);
+        const int grp = a.split_from + (int)(trow / C::QT);
+        const int bh = grp / ntile;
+        const int row = (grp - bh * ntile) * C::QT + (int)(trow % C::QT);
+        if (row >= a.L) continue;
+        float M = -INFINITY;
+        for (int p = 0; p < a.nsplit; ++p) M = fmaxf(M, a.part[((int64_t)p * tail_rows + trow) * REC]);
+        float din = 0.f, dout = 0.f;
+        f32x4 ni = {0.f, 0.f, 0.f, 0.f}, no = {0.f, 0.f, 0.f, 0.f};
+        for (int p = 0; p < a.nsplit; ++p) {
+            const float* rec = a.part + ((int64_t)p * tail_rows + trow) * REC;
+            const f32x4 hd = *(const f32x4*)rec;
+            const float w = hd[0] == -INFINITY ? 0.f : fast_exp2(hd[0] - M);
+            din += w * hd[1];
+            dout += w * hd[2];
+            ni += w * *(const f32x4*)(rec + 4 + 4 * c4);
+            no += w * *(const f32x4*)(rec + 4 + DP + 4 * c4);
+        }
+        const float inv = 1.f / (din + dout);
+        const float inv_in = din > 0.f ? 1.f / din : 0.f;
+        const int bi = bh / a.H, hi = bh - bi * a.H;
+        const int64_t off = (int64_t)bi * a.sb + (int64_t)hi * a.sh + (int64_t)row * a.sl + 4 * c4;
+        float ov[4], rv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            ov[r] = (ni[r] + no[r]) * inv;
+            rv[r] = diff ? ov[r] - ni[r] * inv_in : no[r] * inv;
+        }
+        u32x2 ow, rw;
+        ow[0] = pack_bf16(ov[0], ov[1]);
+        ow[1] = pack_bf16(ov[2], ov[3]);
+        rw[0] = pack_bf16(rv[0], rv[1]);
+        rw[1] = pack_bf16(rv[2], rv[3]);
+        *(u32x2*)((uint16_t*)a.O + off) = ow;
+        *(u32x2*)((uint16_t*)a.R_out + off) = rw;
+        if (c4 == 0) a.rho_out[(int64_t)bh * a.L + row] = din * inv;
+    }
+}
+
+// How the last round is split.  slots = work-groups resident on the whole device at once.  When
+// the groups fill at least one round and leave a last round at most half full, each group of that
+// round is cut into nsplit parts along the key range (at least two key tiles per part, at most
+// 8 parts), so that the last round holds nsplit times as many, shorter, work items.
+struct SplitPlan {
+    int from = 0, nsplit = 1;
+    int64_t groups = 0, tail = 0;
+};
+
+template <int BLOCK, int DP>
+static SplitPlan split_plan(const AttnArgs& a) {
+    using C = CalCfg<DP>;
+    SplitPlan sp;
+    sp.groups = (int64_t)a.B * a.H * ((a.L + C::QT - 1) / C::QT);
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, calib_kernel<BLOCK, DP, true>, C::NT, 0) != hipSuccess)
+        return sp;
+    const int64_t slots = (int64_t)cus * per_cu;
+    if (slots <= 0 || sp.groups < slots) return sp;
+    const int64_t tail = sp.groups % slots;
+    const int64_t nkt = (a.L + 63) / 64;
+    if (tail == 0 || 2 * tail > slots) return sp;
+    const int64_t n = std::min<int64_t>(std::min<int64_t>(slots / tail, 8), nkt / 2);
+    if (n < 2 || sp.groups - tail + tail * n > 0x7fffffff) return sp;
+    sp.from = (int)(sp.groups - tail);
+    sp.nsplit = (int)n;
+    sp.tail = tail;
+    return sp;
+}
+
+template <int BLOCK, int DP>
+static size_t split_bytes(const AttnArgs& a) {
+    const SplitPlan sp = split_plan<BLOCK, DP>(a);
+    if (sp.nsplit <= 1) return 0;
+    return (size_t)sp.nsplit * (size_t)sp.tail * CalCfg<DP>::QT * (4 + 2 * DP) * sizeof(float);
+}
+
 template <int BLOCK, int DP, bool V16>
-static hipError_t launch(AttnArgs a, hipStream_t s) {
+static hipError_t launch(AttnArgs a, float* part, hipStream_t s) {
     using C = CalCfg<DP>;
     const int64_t ntile = (a.L + C::QT - 1) / C::QT;
-    const int64_t G = (int64_t)a.B * a.H * ntile;
+    int64_t G = (int64_t)a.B * a.H * ntile;
     if (G <= 0 || G > 0x7fffffff) return hipErrorInvalidValue;
+    a.nsplit = 1;
+    a.split_from = 0;
+    a.part = nullptr;
+    if (V16 && part) {
+        const SplitPlan sp = split_plan<BLOCK, DP>(a);
+        if (sp.nsplit > 1) {
+            a.split_from = sp.from;
+            a.nsplit = sp.nsplit;
+            a.part = part;
+            G = sp.from + sp.tail * sp.nsplit;
+        }
+    }
     a.G = (int32_t)G;
     hipLaunchKernelGGL((calib_kernel<BLOCK, DP, V16>), dim3((unsigned)G), dim3(C::NT), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.nsplit <= 1) return e;
+    hipLaunchKernelGGL((calib_merge_kernel<DP>), dim3(1024), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -361,7 +509,19 @@ bool calib_supported(const AttnArgs& a, int block) {
     return calib_fast_path(a, block);
 }
 
-hipError_t launch_calib(AttnArgs a, int block, void* v16, hipStream_t s) {
+#define RETTN_CALIB_CASES(X)                                                                    \
+    X(64, 32) X(64, 64) X(64, 96) X(64, 128) X(128, 32) X(128, 64) X(128, 96) X(128, 128)
+
+size_t calib_split_bytes(const AttnArgs& a, int block) {
+    const int dp = pad_d(a.d);
+#define RETTN_CASE(BL, D) \
+    if (block == BL && dp == D) return split_bytes<BL, D>(a);
+    RETTN_CALIB_CASES(RETTN_CASE)
+#undef RETTN_CASE
+    return 0;
+}
+
+hipError_t launch_calib(AttnArgs a, int block, void* v16, void* part, hipStream_t s) {
     const int dp = pad_d(a.d);
     if (v16) {
         hipLaunchKernelGGL(v16_kernel, dim3(2048), dim3(256), 0, s, a, (uint16_t*)v16);
@@ -369,10 +529,10 @@ hipError_t launch_calib(AttnArgs a, int block, void* v16, hipStream_t s) {
         if (e != hipSuccess) return e;
         a.V = v16;
     }
-#define RETTN_CASE(BL, D)                                                                  \
-    if (block == BL && dp == D) return v16 ? launch<BL, D, true>(a, s) : launch<BL, D, false>(a, s);
-    RETTN_CASE(64, 32) RETTN_CASE(64, 64) RETTN_CASE(64, 96) RETTN_CASE(64, 128)
-    RETTN_CASE(128, 32) RETTN_CASE(128, 64) RETTN_CASE(128, 96) RETTN_CASE(128, 128)
+#define RETTN_CASE(BL, D)                                                                         \
+    if (block == BL && dp == D)                                                                   \
+        return v16 ? launch<BL, D, true>(a, (float*)part, s) : launch<BL, D, false>(a, nullptr, s);
+    RETTN_CALIB_CASES(RETTN_CASE)
 #undef RETTN_CASE
     return hipErrorInvalidValue;
 }

@@ -125,18 +125,13 @@ rettn_status calibrate_workspace(const rettn_desc* desc, size_t* bytes) {
     return RETTN_OK;
 }
 
-rettn_status check_calibrate_workspace(const rettn_desc* desc, const void* workspace, size_t workspace_bytes,
-                                       std::initializer_list<const void*> tensors, size_t* need) {
-    if (!need) return RETTN_EINVAL;
-    const rettn_status st = calibrate_workspace(desc, need);
-    if (st != RETTN_OK) return st;
-    if (*need == 0) return RETTN_OK;
-    if (!tensor_ok(workspace) || workspace_bytes < *need) return RETTN_EINVAL;
-    // every tensor spans the same extent in elements as V; the workspace must not touch any of them
-    const size_t esize = desc->dtype == RETTN_BF16 ? 2 : 4;
-    const uintptr_t w0 = (uintptr_t)workspace, w1 = w0 + *need;
+rettn_status check_calibrate_workspace(const void* workspace, size_t workspace_bytes, size_t need,
+                                       size_t tensor_bytes, std::initializer_list<const void*> tensors) {
+    if (need == 0) return RETTN_OK;
+    if (!tensor_ok(workspace) || workspace_bytes < need) return RETTN_EINVAL;
+    const uintptr_t w0 = (uintptr_t)workspace, w1 = w0 + need;
     for (const void* t : tensors) {
-        const uintptr_t t0 = (uintptr_t)t, t1 = t0 + *need / 2 * esize;
+        const uintptr_t t0 = (uintptr_t)t, t1 = t0 + tensor_bytes;
         if (w0 < t1 && t0 < w1) return RETTN_EINVAL;
     }
     return RETTN_OK;

@@ -26,11 +26,11 @@ rettn_status prepare_calibrate(const rettn_desc* desc, const void* Q, const void
 // bad descriptor.
 rettn_status calibrate_workspace(const rettn_desc* desc, size_t* bytes);
 
-// Checks of rettn_calibrate_ws's workspace (after prepare_calibrate): when the call needs one, it
-// must be 16-byte aligned, at least *need bytes and overlap none of the tensors (each spans the
-// descriptor's extent); *need is set to the size.  A workspace the call does not need is ignored.
-rettn_status check_calibrate_workspace(const rettn_desc* desc, const void* workspace, size_t workspace_bytes,
-                                       std::initializer_list<const void*> tensors, size_t* need);
+// Checks of rettn_calibrate_ws's workspace: when need > 0 it must be 16-byte aligned, at least need
+// bytes, and [workspace, workspace + need) must overlap none of the tensors, each tensor_bytes long.
+// A workspace the call does not need (need == 0) is ignored.
+rettn_status check_calibrate_workspace(const void* workspace, size_t workspace_bytes, size_t need,
+                                       size_t tensor_bytes, std::initializer_list<const void*> tensors);
 
 // Checks of rettn_sparse; on RETTN_OK, *args holds the kernel arguments (ramp = 1 + lambda step).
 rettn_status prepare_sparse(const rettn_desc* desc, const void* Q, const void* K, const void* V,

@@ -124,12 +124,11 @@ static void check_calib_workspace() {
         EXPECT(st == RETTN_OK || st == RETTN_EUNSUPPORTED);
         if (st == RETTN_OK) EXPECT(n == (size_t)((e.stride_b + 2 * e.stride_h + 199 * e.stride_l + 64) * 2));
     }
-    const size_t need = (size_t)2 * 3 * 200 * 64 * 2;
+    const size_t need = (size_t)2 * 3 * 200 * 64 * 2 + 4096, tbytes = (size_t)2 * 3 * 200 * 64 * 2;
     const uintptr_t base = (uintptr_t)1 << 40, gap = (uintptr_t)1 << 30;
     const void* t5[5] = {addr(base), addr(base + gap), addr(base + 2 * gap), addr(base + 3 * gap), addr(base + 4 * gap)};
     auto check = [&](uintptr_t ws, size_t bytes) {
-        size_t nd = 0;
-        return host::check_calibrate_workspace(&d, addr(ws), bytes, {t5[0], t5[1], t5[2], t5[3], t5[4]}, &nd);
+        return host::check_calibrate_workspace(addr(ws), bytes, need, tbytes, {t5[0], t5[1], t5[2], t5[3], t5[4]});
     };
     EXPECT(check(base + 8 * gap, need) == RETTN_OK);
     EXPECT(check(base + 8 * gap, need - 1) == RETTN_EINVAL);
@@ -137,11 +136,10 @@ static void check_calib_workspace() {
     EXPECT(check(0, need) == RETTN_EINVAL);
     EXPECT(check(base + 2 * gap, need) == RETTN_EINVAL);                 // V itself
     EXPECT(check(base + gap - need + 16, need) == RETTN_EINVAL);         // ends inside the second tensor
-    EXPECT(check(base + 3 * gap + need - 16, need) == RETTN_EINVAL);     // starts inside the fourth
+    EXPECT(check(base + 3 * gap + tbytes - 16, need) == RETTN_EINVAL);   // starts inside the fourth
     EXPECT(check(base + gap - need, need) == RETTN_OK);                  // just before the second
-    size_t nd = 7;
-    EXPECT(host::check_calibrate_workspace(&f, nullptr, 0, {t5[0]}, &nd) == RETTN_OK && nd == 0);
-    EXPECT(host::check_calibrate_workspace(&d, addr(base + 8 * gap), need, {t5[0]}, nullptr) == RETTN_EINVAL);
+    EXPECT(check(base + 3 * gap + tbytes, need) == RETTN_OK);            // just after the fourth
+    EXPECT(host::check_calibrate_workspace(nullptr, 0, 0, tbytes, {t5[0]}) == RETTN_OK);   // not needed: ignored
 }
 
 static void check_attention_args() {

@@ -286,6 +286,46 @@ def test_calibrate_workspace_path_is_bit_identical(rt, case):
         assert torch.equal(a.view(bits), b.view(bits))
 
 
+def test_calibrate_split_last_round(rt):
+    """A shape whose 8-wave groups (d = 96) fill one round of a 256-CU device and leave a last round
+    of 32 groups: those groups are cut into parts along the key range and merged.  The merged rows
+    match the unsplit path to float32 rounding and the oracle to the usual bar, for both residual
+    kinds; the rows of the whole groups stay bit-identical."""
+    import torch
+    B, H, L, d, block = 1, 18, 4096, 96, 64           # 16 groups of 256 rows per head: 288 groups
+    log(f"case split: B={B} H={H} L={L} d={d} block={block}")
+    q, k, v = make_qkv(B, H, L, d, 41)
+    nb = L // block
+    mask = om.band_mask(nb, 2)
+    idx = rt.index_build(mask, block)
+    tq, tk, tv = (torch.from_numpy(x).to(torch.bfloat16).cuda() for x in (q, k, v))
+    need = rt.calibrate_workspace_bytes(tq, block)
+    v16 = B * H * L * d * 2
+    props = torch.cuda.get_device_properties(0)
+    if props.multi_processor_count == 256:
+        assert need > v16, "a split was expected on a 256-CU device"
+    split_heads = list(range(H - 2, H))               # the last 32 groups are the last two heads
+    rows = sample_rows(L, block, 40, seed=41)
+    for residual in ("masked", "difference"):
+        ref = rt.calibrate(tq, tk, tv, idx, residual=residual, workspace=False)
+        got = rt.calibrate(tq, tk, tv, idx, residual=residual)
+        torch.cuda.synchronize()
+        for what, a, b in zip(("O", "rho", "R"), ref, got):
+            a, b = a.float(), b.float()
+            whole = slice(0, H - 2)
+            assert torch.equal(a[:, whole], b[:, whole]), f"{residual} {what}: whole groups changed"
+            diff = (a - b).abs()
+            assert float(diff.sum() / a.abs().sum().clamp_min(1e-30)) < 1e-4, f"{residual} {what}"
+            assert float(diff.max()) < 4e-3, f"{residual} {what}"
+        if residual == "masked":
+            sub = [x[:, split_heads] for x in (q, k, v)]
+            o_o, rho_o, r_o = oracle.calibrate(*sub, mask, block, rows=rows)
+            o_g, rho_g, r_g = (host(x[:, split_heads][:, :, rows]) for x in got)
+            assert_parity(o_g, o_o, "bf16", "split calibrate O")
+            assert_parity(rho_g, rho_o, "bf16", "split calibrate rho")
+            assert_parity(r_g, r_o, "bf16", "split calibrate R")
+
+
 def test_calibrate_binding_rejects_small_workspace(rt):
     import torch
     q, k, v = (torch.zeros(1, 1, 128, 64, dtype=torch.bfloat16, device="cuda") for _ in range(3))
