@@ -27,6 +27,7 @@ KERNEL_SOURCES = {
     "sparse64_kernel": ["sparse64.hip", "common.h", "attn.h", "args.h"],
     "calib_kernel": ["calib.hip", "common.h", "attn.h", "args.h"],
     "v16_kernel": ["calib.hip", "common.h", "attn.h", "args.h"],
+    "calib_merge_kernel": ["calib.hip", "common.h", "attn.h", "args.h"],
     "attn_bf16_kernel": ["attn_bf16.hip", "common.h", "attn.h", "args.h"],
     "attn_f32_kernel": ["attn_f32.hip", "common.h", "attn.h", "args.h"],
     "sparse_wg_kernel": ["sparse_wg.hip", "common.h", "attn.h", "args.h"],
