@@ -284,6 +284,24 @@ rettn_status rettn_sparse(const rettn_desc* desc, const void* Q, const void* K, 
                           const rettn_index* idx, const float* rho, const void* R,
                           float lambda, int32_t step, void* O, hipStream_t stream);
 
+/* rettn_sparse with a device workspace, into which V is first converted to
+ * float16 (V's own layout, one pass over V) so that the sparse kernel streams
+ * float16 tiles instead of re-encoding each V tile in every query block that
+ * keeps it.  The pass pays when many query blocks keep each key block: it is
+ * taken for bfloat16 with 128-token blocks when idx->nnz is at least 24 times
+ * nkb (each key block kept by 24 query blocks on average); the conversion is
+ * the kernel's own, so O' is bit for bit that of rettn_sparse.
+ * rettn_sparse_workspace_bytes: V's extent in float16 (as for
+ * rettn_calibrate_workspace_bytes, without the 256-byte rounding) when the
+ * pass is taken, else 0; RETTN_EINVAL for a bad descriptor or index.
+ * rettn_sparse_ws: as rettn_sparse; the workspace rules are those of
+ * rettn_calibrate_ws (aligned, large enough, disjoint from Q, K, V, O and R;
+ * ignored when the size is 0). */
+rettn_status rettn_sparse_workspace_bytes(const rettn_desc* desc, const rettn_index* idx, size_t* bytes);
+rettn_status rettn_sparse_ws(const rettn_desc* desc, const void* Q, const void* K, const void* V,
+                             const rettn_index* idx, const float* rho, const void* R, float lambda, int32_t step,
+                             void* workspace, size_t workspace_bytes, void* O, hipStream_t stream);
+
 /* A static string naming a status code. */
 const char* rettn_status_str(rettn_status status);
 

@@ -163,8 +163,29 @@ rettn_status rettn_sparse(const rettn_desc* desc, const void* Q, const void* K, 
     AttnArgs a{};
     const rettn_status st = host::prepare_sparse(desc, Q, K, V, idx, rho, R, lambda, step, O, &a);
     if (st != RETTN_OK) return st;
-    const hipError_t e = desc->dtype == RETTN_BF16 ? rettn::launch_sparse_bf16(a, desc->block, stream)
+    const hipError_t e = desc->dtype == RETTN_BF16 ? rettn::launch_sparse_bf16(a, desc->block, nullptr, stream)
                                                    : rettn::launch_sparse_f32(a, desc->block, stream);
+    return e == hipSuccess ? RETTN_OK : RETTN_EHIP;
+}
+
+rettn_status rettn_sparse_workspace_bytes(const rettn_desc* desc, const rettn_index* idx, size_t* bytes) {
+    return host::sparse_workspace(desc, idx, bytes);
+}
+
+rettn_status rettn_sparse_ws(const rettn_desc* desc, const void* Q, const void* K, const void* V,
+                             const rettn_index* idx, const float* rho, const void* R, float lambda, int32_t step,
+                             void* workspace, size_t workspace_bytes, void* O, hipStream_t stream) {
+    AttnArgs a{};
+    rettn_status st = host::prepare_sparse(desc, Q, K, V, idx, rho, R, lambda, step, O, &a);
+    if (st != RETTN_OK) return st;
+    size_t need = 0;
+    st = host::sparse_workspace(desc, idx, &need);
+    if (st != RETTN_OK) return st;
+    st = host::check_calibrate_workspace(workspace, workspace_bytes, need, need, {Q, K, V, O, R});
+    if (st != RETTN_OK) return st;
+    const hipError_t e = desc->dtype == RETTN_BF16
+                             ? rettn::launch_sparse_bf16(a, desc->block, need ? workspace : nullptr, stream)
+                             : rettn::launch_sparse_f32(a, desc->block, stream);
     return e == hipSuccess ? RETTN_OK : RETTN_EHIP;
 }
 

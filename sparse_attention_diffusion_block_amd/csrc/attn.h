@@ -12,7 +12,9 @@ namespace rettn {
 // calibrations on the 64/128-token-block kernel; ignored by the other paths).  part: null, or
 // calib_split_bytes(a, block) bytes for the partial states of a split last round (with v16 only).
 hipError_t launch_calibrate_bf16(AttnArgs a, int block, void* v16, void* part, hipStream_t s);
-hipError_t launch_sparse_bf16(AttnArgs a, int block, hipStream_t s);
+// v16: null, or device memory covering V's extent for the float16 copy of V (the 128-token-block
+// sparse kernel streams it; the other paths ignore it).
+hipError_t launch_sparse_bf16(AttnArgs a, int block, void* v16, hipStream_t s);
 hipError_t launch_calibrate_f32(AttnArgs a, int block, hipStream_t s);
 hipError_t launch_sparse_f32(AttnArgs a, int block, hipStream_t s);
 
@@ -23,7 +25,10 @@ hipError_t launch_sparse64(AttnArgs a, hipStream_t s);
 // Sparse step for 128-token blocks (bfloat16, d <= 128) and 64-token blocks with d > 64: one
 // work-group of block / 32 waves per query block.
 bool sparse_wg_supported(const AttnArgs& a, int block);
-hipError_t launch_sparse_wg(AttnArgs a, int block, hipStream_t s);
+hipError_t launch_sparse_wg(AttnArgs a, int block, void* v16, hipStream_t s);
+
+// V (bfloat16, a's layout) converted to float16 into v16, same offsets: one pass over V.
+hipError_t launch_v16(const AttnArgs& a, void* v16, hipStream_t s);
 
 // Calibration for 64- and 128-token blocks (bfloat16): 128 or 256 query rows per work-group.  With
 // v16 set, V is first converted to float16 into v16 (same layout) and streamed from there; with

@@ -352,9 +352,9 @@ hipError_t launch_calibrate_bf16(AttnArgs a, int block, void* v16, void* part, h
     if (calib_supported(a, block)) return launch_calib(a, block, v16, part, s);
     return dispatch<true>(a, block, s);
 }
-hipError_t launch_sparse_bf16(AttnArgs a, int block, hipStream_t s) {
+hipError_t launch_sparse_bf16(AttnArgs a, int block, void* v16, hipStream_t s) {
     if (sparse64_supported(a, block)) return launch_sparse64(a, s);
-    if (sparse_wg_supported(a, block)) return launch_sparse_wg(a, block, s);
+    if (sparse_wg_supported(a, block)) return launch_sparse_wg(a, block, v16, s);
     return dispatch<false>(a, block, s);
 }
 

@@ -521,11 +521,15 @@ size_t calib_split_bytes(const AttnArgs& a, int block) {
     return 0;
 }
 
+hipError_t launch_v16(const AttnArgs& a, void* v16, hipStream_t s) {
+    hipLaunchKernelGGL(v16_kernel, dim3(2048), dim3(256), 0, s, a, (uint16_t*)v16);
+    return hipGetLastError();
+}
+
 hipError_t launch_calib(AttnArgs a, int block, void* v16, void* part, hipStream_t s) {
     const int dp = pad_d(a.d);
     if (v16) {
-        hipLaunchKernelGGL(v16_kernel, dim3(2048), dim3(256), 0, s, a, (uint16_t*)v16);
-        const hipError_t e = hipGetLastError();
+        const hipError_t e = launch_v16(a, v16, s);
         if (e != hipSuccess) return e;
         a.V = v16;
     }

@@ -125,6 +125,20 @@ rettn_status calibrate_workspace(const rettn_desc* desc, size_t* bytes) {
     return RETTN_OK;
 }
 
+rettn_status sparse_workspace(const rettn_desc* desc, const rettn_index* idx, size_t* bytes) {
+    if (!desc || !idx || !bytes) return RETTN_EINVAL;
+    rettn_status st = check_desc(desc, idx);
+    if (st != RETTN_OK) return st;
+    *bytes = 0;
+    if (desc->dtype != RETTN_BF16 || desc->block != 128 || idx->nnz < 0) return RETTN_OK;
+    if ((int64_t)idx->nnz < kSparseV16Readers * idx->nkb) return RETTN_OK;
+    size_t v16 = 0;
+    st = calibrate_workspace(desc, &v16);       // V's extent in float16 on the 128-token-block kernel
+    if (st != RETTN_OK) return st;
+    *bytes = v16;
+    return RETTN_OK;
+}
+
 rettn_status check_calibrate_workspace(const void* workspace, size_t workspace_bytes, size_t need,
                                        size_t tensor_bytes, std::initializer_list<const void*> tensors) {
     if (need == 0) return RETTN_OK;

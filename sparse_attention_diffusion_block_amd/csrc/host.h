@@ -26,6 +26,12 @@ rettn_status prepare_calibrate(const rettn_desc* desc, const void* Q, const void
 // bad descriptor.
 rettn_status calibrate_workspace(const rettn_desc* desc, size_t* bytes);
 
+// Workspace of rettn_sparse_ws: the float16 copy of V when the 128-token-block sparse kernel takes
+// the call (bfloat16) and each key block is kept, on average, by at least kSparseV16Readers query
+// blocks (idx->nnz >= that many times nkb), else 0.  RETTN_EINVAL for a bad descriptor or index.
+constexpr int64_t kSparseV16Readers = 24;
+rettn_status sparse_workspace(const rettn_desc* desc, const rettn_index* idx, size_t* bytes);
+
 // Checks of rettn_calibrate_ws's workspace: when need > 0 it must be 16-byte aligned, at least need
 // bytes, and [workspace, workspace + need) must overlap none of the tensors, each tensor_bytes long.
 // A workspace the call does not need (need == 0) is ignored.

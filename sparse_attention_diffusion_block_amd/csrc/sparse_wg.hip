@@ -62,10 +62,11 @@ struct SwgCfg {
     static constexpr int WPE = SB ? 2 : 1;          // resident waves per SIMD to compile for (at least)
 };
 
-template <int BLOCK, int DP>
+template <int BLOCK, int DP, bool V16>
 __global__ void __launch_bounds__((SwgCfg<BLOCK, DP>::NT), 2) __attribute__((amdgpu_waves_per_eu(SwgCfg<BLOCK, DP>::WPE)))
 sparse_wg_kernel(const AttnArgs a) {
     using C = SwgCfg<BLOCK, DP>;
+    static_assert(!(V16 && C::SB), "float16 V tiles are streamed only into double-buffered slots");
     // [buffer][K | V][64 keys][RS]
     __shared__ __attribute__((aligned(1024))) uint16_t lds[C::NBUF * 2 * C::TILE];
 
@@ -106,12 +107,13 @@ sparse_wg_kernel(const AttnArgs a) {
     auto key0 = [&](int t) -> int { return scalar_load(ci, e0 + t / C::TPB) * C::BLOCK + 64 * (t % C::TPB); };
 
     // Tile staging.  K: direct-to-LDS, wave w fills 1 KiB pieces w, w + NW, ...; lane -> (row, physical chunk).
-    // V: thread t holds 16-byte chunks t, t + NT, ... in registers until they are re-encoded and stored.
+    // V, bfloat16: thread t holds 16-byte chunks t, t + NT, ... in registers until they are re-encoded and
+    // stored.  V16 (V already converted to float16 by one pass over it): direct-to-LDS like K.
     // A lane's byte offset within a tile is the same for every tile (a padded chunk takes an offset
     // past every record); the tile's row offset k0 * row_bytes rides in the scalar offset.  (Each
     // offset array is declared right before the lambda that reads it: other placements kept the
     // host compiler from emitting the launch stubs.)
-    u32x4 vreg[C::VC];
+    u32x4 vreg[V16 ? 1 : C::VC];
     uint32_t k_off[C::KL];
 #pragma unroll
     for (int j = 0; j < C::KL; ++j) {
@@ -130,25 +132,40 @@ sparse_wg_kernel(const AttnArgs a) {
                 (uint32_t)k0 * row_bytes, 0, 0);
         }
     };
-    uint32_t v_off[C::VC];
+    uint32_t v_off[V16 ? 1 : C::VC];
 #pragma unroll
-    for (int j = 0; j < C::VC; ++j) {
+    for (int j = 0; j < (V16 ? 0 : C::VC); ++j) {
         const int id = tid + j * C::NT;
         const int r = id / C::CPR;
         const int c = (id % C::CPR) ^ swz(r);
         v_off[j] = c * 8 < a.d ? (uint32_t)r * row_bytes + 16u * c : kOOB;
     }
-    auto issue_v = [&](int k0) {
+    // V tile at key k0 towards slot buf (bfloat16: into registers now, into the slot at store_v)
+    auto issue_v = [&](int k0, int buf) {
+        if constexpr (V16) {
 #pragma unroll
-        for (int j = 0; j < C::VC; ++j) {
-            vreg[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, v_off[j], (uint32_t)k0 * row_bytes, 0));
+            for (int j = 0; j < C::KL; ++j) {
+                const int piece = wave + j * C::NW;
+                const uint32_t off = k_off[j];
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rv, (__attribute__((address_space(3))) void*)(lds + buf * 2 * C::TILE + C::TILE + piece * 512), 16,
+                    off, (uint32_t)k0 * row_bytes, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < C::VC; ++j) {
+                const uint32_t off = v_off[j];
+                vreg[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, (uint32_t)k0 * row_bytes, 0));
+            }
         }
     };
     auto store_v = [&](int buf) {
+        if constexpr (!V16) {
 #pragma unroll
-        for (int j = 0; j < C::VC; ++j) {
-            const int id = tid + j * C::NT;
-            *(u32x4*)(lds + buf * 2 * C::TILE + C::TILE + id * 8) = bf16x8_to_f16x8(vreg[j]);
+            for (int j = 0; j < C::VC; ++j) {
+                const int id = tid + j * C::NT;
+                *(u32x4*)(lds + buf * 2 * C::TILE + C::TILE + id * 8) = bf16x8_to_f16x8(vreg[j]);
+            }
         }
     };
 
@@ -166,7 +183,7 @@ sparse_wg_kernel(const AttnArgs a) {
     if (ntiles > 0) {
         kcur = key0(0);
         issue_k(kcur, 0);
-        issue_v(kcur);
+        issue_v(kcur, 0);
         store_v(0);
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         __syncthreads();
@@ -178,7 +195,7 @@ sparse_wg_kernel(const AttnArgs a) {
         const int knext = more ? key0(t + 1) : 0;
         if (more) {
             if constexpr (!C::SB) issue_k(knext, buf ^ 1);
-            issue_v(knext);
+            issue_v(knext, buf ^ 1);                // (single slot: into registers, stored after the barrier)
         }
         const uint16_t* ks = lds + buf * 2 * C::TILE;
         const uint16_t* vs = ks + C::TILE;
@@ -303,13 +320,13 @@ sparse_wg_kernel(const AttnArgs a) {
         }
 }
 
-template <int BLOCK, int DP>
+template <int BLOCK, int DP, bool V16>
 static hipError_t launch(AttnArgs a, hipStream_t s) {
     using C = SwgCfg<BLOCK, DP>;
     const int64_t G = (int64_t)a.B * a.H * a.nqb;
     if (G <= 0 || G > 0x7fffffff) return hipErrorInvalidValue;
     a.G = (int32_t)G;
-    hipLaunchKernelGGL((sparse_wg_kernel<BLOCK, DP>), dim3((unsigned)G), dim3(C::NT), 0, s, a);
+    hipLaunchKernelGGL((sparse_wg_kernel<BLOCK, DP, V16>), dim3((unsigned)G), dim3(C::NT), 0, s, a);
     return hipGetLastError();
 }
 
@@ -318,13 +335,24 @@ bool sparse_wg_supported(const AttnArgs& a, int block) {
     return (block == 128 || (block == 64 && a.d > 64)) && a.d <= 128 && slice_offsets_fit(a);
 }
 
-hipError_t launch_sparse_wg(AttnArgs a, int block, hipStream_t s) {
-    if (block == 64) return pad_d(a.d) <= 96 ? launch<64, 96>(a, s) : launch<64, 128>(a, s);
+hipError_t launch_sparse_wg(AttnArgs a, int block, void* v16, hipStream_t s) {
+    if (block == 64) return pad_d(a.d) <= 96 ? launch<64, 96, false>(a, s) : launch<64, 128, false>(a, s);
+    if (v16) {
+        const hipError_t e = launch_v16(a, v16, s);
+        if (e != hipSuccess) return e;
+        a.V = v16;
+        switch (pad_d(a.d)) {
+            case 32: return launch<128, 32, true>(a, s);
+            case 64: return launch<128, 64, true>(a, s);
+            case 96: return launch<128, 96, true>(a, s);
+            default: return launch<128, 128, true>(a, s);
+        }
+    }
     switch (pad_d(a.d)) {
-        case 32: return launch<128, 32>(a, s);
-        case 64: return launch<128, 64>(a, s);
-        case 96: return launch<128, 96>(a, s);
-        default: return launch<128, 128>(a, s);
+        case 32: return launch<128, 32, false>(a, s);
+        case 64: return launch<128, 64, false>(a, s);
+        case 96: return launch<128, 96, false>(a, s);
+        default: return launch<128, 128, false>(a, s);
     }
 }
 

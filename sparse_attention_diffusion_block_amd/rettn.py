@@ -17,7 +17,8 @@ MASK_DIAG, MASK_BAND, MASK_COGVIDEO3D, MASK_FULL = 0, 1, 2, 3
 RESIDUAL_MASKED, RESIDUAL_DIFFERENCE = 0, 1
 EXPORTED = ("rettn_mask_build", "rettn_index_build", "rettn_index_build_sliced", "rettn_dynamic_workspace_bytes",
             "rettn_dynamic_index", "rettn_dynamic_index_noalloc", "rettn_calibrate", "rettn_calibrate_residual",
-            "rettn_calibrate_workspace_bytes", "rettn_calibrate_ws", "rettn_sparse", "rettn_status_str")
+            "rettn_calibrate_workspace_bytes", "rettn_calibrate_ws", "rettn_sparse", "rettn_sparse_workspace_bytes",
+            "rettn_sparse_ws", "rettn_status_str")
 STATUS_ESCRATCH = 4
 NOALLOC_SCRATCH_BYTES = 32 << 20   # RETTN_NOALLOC_SCRATCH_BYTES
 
@@ -87,6 +88,12 @@ def lib():
         L.rettn_sparse.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, ctypes.POINTER(Index), vp, vp,
                                    ctypes.c_float, i32, vp, vp]
         L.rettn_sparse.restype = ctypes.c_int
+        L.rettn_sparse_workspace_bytes.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Index),
+                                                   ctypes.POINTER(ctypes.c_size_t)]
+        L.rettn_sparse_workspace_bytes.restype = ctypes.c_int
+        L.rettn_sparse_ws.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, ctypes.POINTER(Index), vp, vp,
+                                      ctypes.c_float, i32, vp, ctypes.c_size_t, vp, vp]
+        L.rettn_sparse_ws.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -309,8 +316,22 @@ def calibrate(q, k, v, index, out=None, residual="masked", workspace=None):
     return o, rho, r
 
 
-def sparse(q, k, v, index, rho, r, lam=0.04, step=1, out=None):
-    """Sparse step `step` after a calibration: min(1, rho (1 + lam step)) * window attention + R."""
+def sparse_workspace_bytes(q, index):
+    """Device workspace (bytes) rettn_sparse_ws takes for tensors like q and this index (0: none)."""
+    desc = _desc(q, index.block)
+    idx = index.c_struct()
+    n = ctypes.c_size_t(0)
+    _check(lib().rettn_sparse_workspace_bytes(ctypes.byref(desc), ctypes.byref(idx), ctypes.byref(n)),
+           "rettn_sparse_workspace_bytes")
+    return int(n.value)
+
+
+def sparse(q, k, v, index, rho, r, lam=0.04, step=1, out=None, workspace=None):
+    """Sparse step `step` after a calibration: min(1, rho (1 + lam step)) * window attention + R.
+
+    workspace: None allocates what rettn_sparse_ws takes (V in float16, only for dense 128-token-block
+    indices; usually nothing); a uint8 tensor of at least sparse_workspace_bytes(q, index) bytes is
+    used as given; False calls rettn_sparse, which takes no workspace (same results)."""
     import torch
     q, k, v, r = _prep((q, k, v, r))
     _check_rho(rho, q)
@@ -319,7 +340,21 @@ def sparse(q, k, v, index, rho, r, lam=0.04, step=1, out=None):
     o = out if out is not None else torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
     desc = _desc(q, index.block)
     idx = index.c_struct()
-    _check(lib().rettn_sparse(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(idx),
-                              rho.data_ptr(), r.data_ptr(), float(lam), int(step), o.data_ptr(), _stream(q.device)),
-           "rettn_sparse")
+    if workspace is False:
+        _check(lib().rettn_sparse(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(idx),
+                                  rho.data_ptr(), r.data_ptr(), float(lam), int(step), o.data_ptr(),
+                                  _stream(q.device)), "rettn_sparse")
+        return o
+    need = sparse_workspace_bytes(q, index)
+    ws_ptr, ws_bytes = None, 0
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        elif (not workspace.is_cuda or workspace.device != q.device or workspace.dtype != torch.uint8
+              or not workspace.is_contiguous() or workspace.numel() < need):
+            raise ValueError(f"workspace must be a contiguous uint8 tensor of at least {need} bytes on Q's device")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    _check(lib().rettn_sparse_ws(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(idx),
+                                 rho.data_ptr(), r.data_ptr(), float(lam), int(step), ws_ptr, ws_bytes, o.data_ptr(),
+                                 _stream(q.device)), "rettn_sparse_ws")
     return o

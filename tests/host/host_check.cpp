@@ -140,6 +140,23 @@ static void check_calib_workspace() {
     EXPECT(check(base + gap - need, need) == RETTN_OK);                  // just before the second
     EXPECT(check(base + 3 * gap + tbytes, need) == RETTN_OK);            // just after the fourth
     EXPECT(host::check_calibrate_workspace(nullptr, 0, 0, tbytes, {t5[0]}) == RETTN_OK);   // not needed: ignored
+
+    // the sparse step's pass: 128-token blocks whose key blocks are kept by enough query blocks
+    rettn_desc s128 = {1, 2, 128 * 60, 128, 128, RETTN_BF16, 2 * 128 * 60 * 128, 128 * 60 * 128, 128};
+    rettn_index ix{};
+    ix.nqb = ix.nkb = 60;
+    ix.nnz = (int32_t)(host::kSparseV16Readers * 60);
+    EXPECT(host::sparse_workspace(&s128, &ix, &n) == RETTN_OK && n == (size_t)2 * 128 * 60 * 128 * 2);
+    ix.nnz -= 1;
+    EXPECT(host::sparse_workspace(&s128, &ix, &n) == RETTN_OK && n == 0);
+    ix.nnz = INT32_MAX;
+    EXPECT(host::sparse_workspace(&s128, &ix, &n) == RETTN_OK && n == (size_t)2 * 128 * 60 * 128 * 2);
+    s128.block = 64;
+    ix.nqb = ix.nkb = 120;
+    EXPECT(host::sparse_workspace(&s128, &ix, &n) == RETTN_OK && n == 0);
+    EXPECT(host::sparse_workspace(nullptr, &ix, &n) == RETTN_EINVAL);
+    EXPECT(host::sparse_workspace(&s128, nullptr, &n) == RETTN_EINVAL);
+    EXPECT(host::sparse_workspace(&s128, &ix, nullptr) == RETTN_EINVAL);
 }
 
 static void check_attention_args() {

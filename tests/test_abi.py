@@ -239,6 +239,47 @@ def test_calibrate_ws_rejects_bad_workspaces():
     assert call(q=FAKE + 8) == EINVAL
 
 
+def test_sparse_workspace_size():
+    """V's extent in float16 only for 128-token blocks whose key blocks are each kept by 24 query blocks
+    on average (nnz >= 24 nkb); 0 otherwise."""
+    lib = rt.lib()
+
+    def size(d, nnz):
+        n = ctypes.c_size_t(7)
+        nb = -(-d.L // d.block)
+        idx = b.Index(nb, nb, nnz, FAKE, FAKE, FAKE)
+        return lib.rettn_sparse_workspace_bytes(ctypes.byref(d), ctypes.byref(idx), ctypes.byref(n)), n.value
+    d = b.Desc(1, 2, 128 * 60, 128, 128, b.RETTN_BF16, 2 * 128 * 60 * 128, 128 * 60 * 128, 128)
+    assert size(d, 24 * 60) == (0, 2 * 128 * 60 * 128 * 2)
+    assert size(d, 24 * 60 - 1) == (0, 0)
+    d64 = b.Desc(1, 2, 128 * 60, 128, 64, b.RETTN_BF16, 2 * 128 * 60 * 128, 128 * 60 * 128, 128)
+    assert size(d64, 120 * 120) == (0, 0)              # 64-token blocks never take the pass
+    f32 = b.Desc(1, 2, 128 * 60, 128, 128, b.RETTN_F32, 2 * 128 * 60 * 128, 128 * 60 * 128, 128)
+    assert size(f32, 60 * 60) == (0, 0)
+    bad = b.Desc(1, 2, 128 * 60, 0, 128, b.RETTN_BF16, 2 * 128 * 60 * 128, 128 * 60 * 128, 128)
+    assert size(bad, 60 * 60)[0] == EINVAL
+    assert lib.rettn_sparse_workspace_bytes(ctypes.byref(d), None, ctypes.byref(ctypes.c_size_t())) == EINVAL
+
+
+def test_sparse_ws_rejects_bad_workspaces():
+    lib = rt.lib()
+    L, nb = 128 * 60, 60
+    d = b.Desc(1, 2, L, 128, 128, b.RETTN_BF16, 2 * L * 128, L * 128, 128)
+    need = 2 * L * 128 * 2
+    idx = b.Index(nb, nb, nb * nb, FAKE, FAKE, FAKE)
+    base = 1 << 40
+    q, k, v, o, r, rho = (base + i * (1 << 30) for i in range(6))
+
+    def call(ws, ws_bytes, lam=0.04):
+        return lib.rettn_sparse_ws(ctypes.byref(d), q, k, v, ctypes.byref(idx), rho, r, lam, 1, ws, ws_bytes, o, None)
+    ws_ok = base + 8 * (1 << 30)
+    assert call(None, need) == EINVAL
+    assert call(ws_ok + 8, need) == EINVAL
+    assert call(ws_ok, need - 1) == EINVAL
+    assert call(k + 16, need) == EINVAL                 # overlaps K
+    assert call(ws_ok, need, lam=-1.0) == EINVAL
+
+
 def test_dynamic_index_rejects_bad_arguments():
     lib = rt.lib()
     d = _good_desc()

@@ -326,6 +326,31 @@ def test_calibrate_split_last_round(rt):
             assert_parity(r_g, r_o, "bf16", "split calibrate R")
 
 
+@pytest.mark.parametrize("L,d,mask_kind", [(128 * 56, 128, "full"), (128 * 50 - 17, 96, "full"),
+                                         (128 * 64, 64, "band")])
+def test_sparse_workspace_path_is_bit_identical(rt, L, d, mask_kind):
+    """With many query blocks per key block, rettn_sparse_ws converts V to float16 once and the
+    128-token-block kernel streams it: O' bit for bit that of rettn_sparse, and the oracle's."""
+    import torch
+    B, H, block = 1, 2, 128
+    log(f"case sparse ws: B={B} H={H} L={L} d={d} block={block} mask={mask_kind}")
+    q, k, v = make_qkv(B, H, L, d, 51)
+    nb = -(-L // block)
+    mask = om.full_mask(nb) if mask_kind == "full" else om.band_mask(nb, 25)
+    idx = rt.index_build(mask, block)
+    tq, tk, tv = (torch.from_numpy(x).to(torch.bfloat16).cuda() for x in (q, k, v))
+    assert rt.sparse_workspace_bytes(tq, idx) == B * H * L * d * 2
+    rho_c, r_c = make_cache(B, H, L, d, seed=51)
+    trho, tr = torch.from_numpy(rho_c).cuda(), torch.from_numpy(r_c).to(torch.bfloat16).cuda()
+    ref = rt.sparse(tq, tk, tv, idx, trho, tr, lam=0.04, step=2, workspace=False)
+    got = rt.sparse(tq, tk, tv, idx, trho, tr, lam=0.04, step=2)
+    torch.cuda.synchronize()
+    assert torch.equal(ref.view(torch.int16), got.view(torch.int16))
+    rows = sample_rows(L, block, 24, seed=51)
+    o_o = oracle.sparse_step(q, k, v, mask, block, rho_c[:, :, rows], r_c[:, :, rows], 0.04, 2, rows=rows)
+    assert_parity(host(got[:, :, rows]), o_o, "bf16", "sparse O' (workspace path)")
+
+
 def test_calibrate_binding_rejects_small_workspace(rt):
     import torch
     q, k, v = (torch.zeros(1, 1, 128, 64, dtype=torch.bfloat16, device="cuda") for _ in range(3))
