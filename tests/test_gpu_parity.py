@@ -286,16 +286,25 @@ def test_calibrate_workspace_path_is_bit_identical(rt, case):
         assert torch.equal(a.view(bits), b.view(bits))
 
 
-def test_calibrate_split_last_round(rt):
-    """A shape whose 8-wave groups (d = 96) fill one round of a 256-CU device and leave a last round
-    of 32 groups: those groups are cut into parts along the key range and merged.  The merged rows
-    match the unsplit path to float32 rounding and the oracle to the usual bar, for both residual
-    kinds; the rows of the whole groups stay bit-identical."""
+SPLIT_CASES = [
+    # B, H, L, d, block, heads holding the split groups (on a 256-CU device)
+    (1, 18, 4096, 96, 64, 2),      # 8-wave groups of 256 rows, one per CU: 288 groups, 32 split
+    (1, 26, 4096, 64, 64, 2),      # 4-wave groups of 128 rows, three per CU: 832 groups, 64 split
+    (1, 18, 3840 - 40, 128, 128, 1),   # d = 128, 128-token blocks, a ragged tail: 270 groups, 14 split
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[f"d{c[3]}-b{c[4]}-H{c[1]}" for c in SPLIT_CASES])
+def test_calibrate_split_last_round(rt, case):
+    """Shapes whose groups fill one round of a 256-CU device and leave a short last round: those
+    groups are cut into parts along the key range and merged.  The merged rows match the unsplit
+    path to float32 rounding and the oracle to the usual bar, for both residual kinds; the rows of
+    the whole groups stay bit-identical."""
     import torch
-    B, H, L, d, block = 1, 18, 4096, 96, 64           # 16 groups of 256 rows per head: 288 groups
+    B, H, L, d, block, nsplit_heads = case
     log(f"case split: B={B} H={H} L={L} d={d} block={block}")
     q, k, v = make_qkv(B, H, L, d, 41)
-    nb = L // block
+    nb = -(-L // block)
     mask = om.band_mask(nb, 2)
     idx = rt.index_build(mask, block)
     tq, tk, tv = (torch.from_numpy(x).to(torch.bfloat16).cuda() for x in (q, k, v))
@@ -304,7 +313,7 @@ def test_calibrate_split_last_round(rt):
     props = torch.cuda.get_device_properties(0)
     if props.multi_processor_count == 256:
         assert need > v16, "a split was expected on a 256-CU device"
-    split_heads = list(range(H - 2, H))               # the last 32 groups are the last two heads
+    split_heads = list(range(H - nsplit_heads, H))    # the split groups lie in the last heads
     rows = sample_rows(L, block, 40, seed=41)
     for residual in ("masked", "difference"):
         ref = rt.calibrate(tq, tk, tv, idx, residual=residual, workspace=False)
@@ -312,7 +321,7 @@ def test_calibrate_split_last_round(rt):
         torch.cuda.synchronize()
         for what, a, b in zip(("O", "rho", "R"), ref, got):
             a, b = a.float(), b.float()
-            whole = slice(0, H - 2)
+            whole = slice(0, H - nsplit_heads)
             assert torch.equal(a[:, whole], b[:, whole]), f"{residual} {what}: whole groups changed"
             diff = (a - b).abs()
             assert float(diff.sum() / a.abs().sum().clamp_min(1e-30)) < 1e-4, f"{residual} {what}"
