@@ -14,9 +14,15 @@
 //     rows, 32 per wave, and walks all key tiles of 64 keys, so each K/V tile
 //     fetched from L2 feeds 128 (256) rows; at d <= 64 three work-groups share
 //     a CU, which keeps three waves per SIMD issuing the softmax's vector work;
-//   * K tiles arrive by coalesced direct-to-LDS loads; V tiles by coalesced
-//     16-byte loads that are re-encoded to float16 once per work-group and
-//     written to LDS; both double buffered, one barrier per tile;
+//   * K tiles arrive by coalesced direct-to-LDS loads; V tiles either the same
+//     way from a float16 copy of V made by one pass over it (v16_kernel, when
+//     the caller supplies a workspace), or by coalesced 16-byte loads that are
+//     re-encoded to float16 once per work-group and written to LDS; both double
+//     buffered, one barrier per tile;
+//   * with a workspace, a last round of work-groups at most half full is split
+//     along the key range: each part stores its partial softmax state and
+//     calib_merge_kernel combines them (a tail of 12% of a round otherwise
+//     costs a whole round);
 //   * S^T = K Q^T and O^T += V^T P^T on 32x32x16 MFMA (bf16, then fp16), one
 //     query row per lane; V^T fragments come from the transposing LDS read;
 //   * the static mask bit of (query block, key block) is wave-uniform and

@@ -10,7 +10,9 @@
 // Design for gfx950: one work-group of 4 waves per 128-row query block, 32
 // rows per wave, walks the block's CSR row 64 keys at a time.  K tiles arrive
 // by coalesced direct-to-LDS loads; V tiles by coalesced 16-byte loads that are
-// re-encoded to float16 once per work-group; both double buffered, one barrier
+// re-encoded to float16 once per work-group, or, when many query blocks keep
+// each key block and the caller supplies a workspace, direct-to-LDS from a
+// float16 copy of V made by one pass over it; both double buffered, one barrier
 // per tile.  One accumulator set and Q in registers keep a wave at about 200
 // registers, so two work-groups share a CU (2 waves per SIMD, 128 KiB of LDS):
 // a SIMD issues the softmax's vector work faster the more waves it holds.  The
