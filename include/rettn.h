@@ -258,7 +258,8 @@ rettn_status rettn_calibrate_residual(const rettn_desc* desc, const void* Q, con
  * rettn_calibrate_ws: as rettn_calibrate_residual, with the size queried while
  * the same device is current.  When that size is not 0 the workspace must be
  * 16-byte aligned, at least that size and overlap none of Q, K, V, O and R
- * (each taken over V's extent), else RETTN_EINVAL with nothing launched; when
+ * (each taken over V's extent) nor rho (B H L floats), else RETTN_EINVAL with
+ * nothing launched; when
  * it is 0 the workspace is ignored (it may be null).  The caller owns the
  * workspace; its contents before and after the call mean nothing.  Two or
  * three launches on `stream`, no allocation and no host wait, so the call can
@@ -295,8 +296,8 @@ rettn_status rettn_sparse(const rettn_desc* desc, const void* Q, const void* K, 
  * rettn_calibrate_workspace_bytes, without the 256-byte rounding) when the
  * pass is taken, else 0; RETTN_EINVAL for a bad descriptor or index.
  * rettn_sparse_ws: as rettn_sparse; the workspace rules are those of
- * rettn_calibrate_ws (aligned, large enough, disjoint from Q, K, V, O and R;
- * ignored when the size is 0). */
+ * rettn_calibrate_ws (aligned, large enough, disjoint from Q, K, V, O, R and
+ * rho; ignored when the size is 0). */
 rettn_status rettn_sparse_workspace_bytes(const rettn_desc* desc, const rettn_index* idx, size_t* bytes);
 rettn_status rettn_sparse_ws(const rettn_desc* desc, const void* Q, const void* K, const void* V,
                              const rettn_index* idx, const float* rho, const void* R, float lambda, int32_t step,

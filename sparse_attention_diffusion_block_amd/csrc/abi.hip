@@ -56,6 +56,9 @@ rettn_status calib_workspace(const rettn_desc* desc, CalibWorkspace* w) {
     return RETTN_OK;
 }
 
+// bytes of rho: one float per (batch, head, row); the descriptor has been validated (B H L < 2^40)
+size_t rho_bytes(const rettn_desc* desc) { return (size_t)desc->B * desc->H * desc->L * sizeof(float); }
+
 }  // namespace
 
 extern "C" {
@@ -150,6 +153,8 @@ rettn_status rettn_calibrate_ws(const rettn_desc* desc, const void* Q, const voi
     if (st != RETTN_OK) return st;
     st = host::check_calibrate_workspace(workspace, workspace_bytes, w.total, w.v16, {Q, K, V, O, R});
     if (st != RETTN_OK) return st;
+    st = host::check_calibrate_workspace(workspace, workspace_bytes, w.total, rho_bytes(desc), {rho});
+    if (st != RETTN_OK) return st;
     void* v16 = w.total ? workspace : nullptr;
     void* part = w.part ? (char*)workspace + w.part_offset : nullptr;
     const hipError_t e = desc->dtype == RETTN_BF16 ? rettn::launch_calibrate_bf16(a, desc->block, v16, part, stream)
@@ -182,6 +187,8 @@ rettn_status rettn_sparse_ws(const rettn_desc* desc, const void* Q, const void* 
     st = host::sparse_workspace(desc, idx, &need);
     if (st != RETTN_OK) return st;
     st = host::check_calibrate_workspace(workspace, workspace_bytes, need, need, {Q, K, V, O, R});
+    if (st != RETTN_OK) return st;
+    st = host::check_calibrate_workspace(workspace, workspace_bytes, need, rho_bytes(desc), {rho});
     if (st != RETTN_OK) return st;
     const hipError_t e = desc->dtype == RETTN_BF16
                              ? rettn::launch_sparse_bf16(a, desc->block, need ? workspace : nullptr, stream)

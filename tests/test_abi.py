@@ -232,6 +232,8 @@ def test_calibrate_ws_rejects_bad_workspaces():
     assert call(ws=v) == EINVAL                       # the workspace is V itself
     assert call(ws=o + need - 16) == EINVAL           # its first bytes overlap O's last ones
     assert call(ws=q - need + 16) == EINVAL           # its last bytes overlap Q's first ones
+    assert call(ws=rho + 2 * 3 * 200 * 4 - 16) == EINVAL   # overlaps the last floats of rho
+    assert call(ws=rho - need + 16) == EINVAL         # its last bytes overlap rho's first ones
     assert call(kind=7) == EINVAL
     bad = _good_desc()
     bad.d = 0
@@ -277,6 +279,7 @@ def test_sparse_ws_rejects_bad_workspaces():
     assert call(ws_ok + 8, need) == EINVAL
     assert call(ws_ok, need - 1) == EINVAL
     assert call(k + 16, need) == EINVAL                 # overlaps K
+    assert call(rho + 16, need) == EINVAL               # overlaps rho (read after the conversion pass)
     assert call(ws_ok, need, lam=-1.0) == EINVAL
 
 
