@@ -5,7 +5,7 @@
     python -m sparse_attention_diffusion_block_amd.measure peaks
     python -m sparse_attention_diffusion_block_amd.measure dynamic  [--runs 50] [--keep 9]
     python -m sparse_attention_diffusion_block_amd.measure graph    [--runs 50]
-    python -m sparse_attention_diffusion_block_amd.measure kernels  --config N [--runs 3]
+    python -m sparse_attention_diffusion_block_amd.measure kernels  --config N [--runs 3] [--mask I]
 
 sweep    the sparse step on the shapes of the CogVideoX-2B-like workload (B=2, H=30,
          L=17776, d=64, block 64) under band windows of 75 / 87.5 / 93.8 / 96.9% block
@@ -21,8 +21,9 @@ dynamic  on the CogVideoX-2B-like shapes: the dynamic block-mask index (block me
 graph    wall time of one refresh period (a calibration and the sparse steps until the next
          one, outputs preallocated) on the image and video workloads, launched eagerly from
          Python and replayed from a HIP graph: what the host's launch path costs per period.
-kernels  the calibration and the sparse step of one workload (every mask), `--runs` calls
-         each, nothing timed: the program a counter-collecting profiler runs.
+kernels  the calibration and the sparse step of one workload (every mask, or the one `--mask`
+         selects), `--runs` calls each, nothing timed: the program a counter-collecting
+         profiler runs.
 peaks    a measured matrix peak (a large bfloat16 GEMM through the vendor library) and
          a measured copy bandwidth, beside the datasheet figures.
 
@@ -269,7 +270,8 @@ def cmd_kernels(args):
     base, drifted, rho, r = _inputs(cfg)
     q, k, v = base
     o, rh, rr, o2 = torch.empty_like(q), torch.empty_like(rho), torch.empty_like(q), torch.empty_like(q)
-    for spec in cfg.masks:
+    masks = cfg.masks if args.mask is None else (cfg.masks[args.mask],)
+    for spec in masks:
         idx = rt.index_build(rt.mask_build(spec.kind, spec.nb, spec.w, spec.text_blocks, spec.tshift), cfg.block)
         for _ in range(args.runs):
             rt.calibrate(q, k, v, idx, out=(o, rh, rr))
@@ -307,6 +309,7 @@ def main(argv=None):
         sp.add_argument("--runs", type=int, default=3 if name == "kernels" else 50)
         if name == "kernels":
             sp.add_argument("--config", type=int, required=True)
+            sp.add_argument("--mask", type=int, default=None, help="only this mask of the workload (0-based)")
         if name == "dynamic":
             sp.add_argument("--keep", type=int, default=9)
     args = ap.parse_args(argv)
