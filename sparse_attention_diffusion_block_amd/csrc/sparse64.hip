@@ -16,7 +16,9 @@
 //     the buffer bounds.  K comes back as the A fragments of S^T = K Q^T, V
 //     through the transposing LDS read as the V^T fragments of
 //     O^T += V^T P^T.  Each slot is refilled with the next key block as soon
-//     as its fragments are in registers;
+//     as its fragments are in registers.  Q, R and O, touched once, move as
+//     non-temporal whole rows; K and V keep the default policy, since L2
+//     serves their reuse across query blocks;
 //   * the MFMAs of one row tile are interleaved with independent vector work
 //     (the float16 re-encoding of V, the probabilities of the other row
 //     tile), which a wave issues while its MFMAs execute;
@@ -36,6 +38,11 @@ namespace rettn {
 namespace {
 
 constexpr uint32_t kOOB = 0x80000000u;   // a buffer offset past every record: reads as zero
+// Cache policy of the streamed tiles: Q and R are read once and O written once, as whole 128-byte
+// rows, so they move non-temporally (the nt bit) and leave the L2 to the K and V blocks that later
+// query blocks of the head read again.
+constexpr int kStream = 2;
+constexpr int kReused = 0;
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -108,16 +115,16 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // (plain expressions only inside these loaders: a lambda called from another
     // lambda here, a buffer-resource lambda parameter or a generic pointer cast to
     // the LDS address space keeps the host compiler from emitting the launch stub)
-#define RETTN_TILE_LOADER(NAME, RSRC, SLOT)                                                                   \
+#define RETTN_TILE_LOADER(NAME, RSRC, SLOT, POLICY)                                                           \
     auto NAME = [&](int row0) {                                                                                  \
         _Pragma("unroll") for (int i = 0; i < C::NL; ++i)                                                         \
             __builtin_amdgcn_raw_ptr_buffer_load_lds(RSRC, (__attribute__((address_space(3))) void*)(SLOT + i * 512), \
-                                                     16, lane_off, RETTN_ROW_OFF(row0, i), 0, 0);               \
+                                                     16, lane_off, RETTN_ROW_OFF(row0, i), 0, POLICY);          \
     };
-    RETTN_TILE_LOADER(load_q, rq, vslot)
-    RETTN_TILE_LOADER(load_k, rk, kslot)
-    RETTN_TILE_LOADER(load_v, rv, vslot)
-    RETTN_TILE_LOADER(load_r, rr, vslot)
+    RETTN_TILE_LOADER(load_q, rq, vslot, kStream)
+    RETTN_TILE_LOADER(load_k, rk, kslot, kReused)
+    RETTN_TILE_LOADER(load_v, rv, vslot, kReused)
+    RETTN_TILE_LOADER(load_r, rr, vslot, kStream)
 #undef RETTN_TILE_LOADER
     // fragment of row r, logical chunk c (16 bytes)
     auto frag = [&](const uint16_t* slot, int r, int c) -> u32x4 {
@@ -360,7 +367,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
     for (int i = 0; i < C::NL; ++i) {
         const u32x4 w = *(const u32x4*)(vslot + (8 * i + trow) * C::RS + tpc * 8);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), ro, lane_off, RETTN_ROW_OFF(q0, i), 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), ro, lane_off, RETTN_ROW_OFF(q0, i), kStream);
     }
 #undef RETTN_ROW_OFF
 }
