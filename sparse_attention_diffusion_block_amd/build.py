@@ -2,8 +2,8 @@
 
 Each HIP source is compiled to an object in parallel, then linked into a
 shared library that sits next to this file, where the binding loads it.
-The issue-cost probe (a standalone measurement program, not part of the
-library) is built beside it as `probe_issue`.
+The issue-cost and HBM streaming probes (standalone measurement programs, not
+part of the library) are built beside it as `probe_issue` and `probe_stream`.
 """
 import os
 import shutil
@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librettn.so")
-PROBE = os.path.join(HERE, "probe_issue")
+PROBES = [os.path.join(HERE, "probe_issue"), os.path.join(HERE, "probe_stream")]
 SOURCES = ["host.cpp", "abi.hip", "attn_bf16.hip", "attn_f32.hip", "index.hip", "sparse64.hip", "calib.hip", "dynamic.hip", "sparse_wg.hip"]
 ARCH = "gfx950"
 # Packed fp32 instructions are disabled in all device code.
@@ -44,7 +44,8 @@ def build(verbose=False):
     os.makedirs(OBJ, exist_ok=True)
     objs = [os.path.join(OBJ, os.path.splitext(s)[0] + ".o") for s in SOURCES]
     cmds = [[hipcc, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
-    cmds.append([hipcc, *FLAGS, os.path.join(CSRC, "probe_issue.hip"), "-o", PROBE + ".tmp"])
+    for probe in PROBES:
+        cmds.append([hipcc, *FLAGS, os.path.join(CSRC, os.path.basename(probe) + ".hip"), "-o", probe + ".tmp"])
     with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():
@@ -53,7 +54,8 @@ def build(verbose=False):
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     _check_launch_stubs(tmp)
     os.replace(tmp, LIB)
-    os.replace(PROBE + ".tmp", PROBE)
+    for probe in PROBES:
+        os.replace(probe + ".tmp", probe)
     return LIB
 
 
