@@ -25,7 +25,9 @@
 // the group keeps a single K and V slot (32 KiB instead of 64) and is compiled
 // for two waves per SIMD, so four groups share a CU: with two or four kept
 // blocks per row there is little to double buffer, and the doubled residency
-// pays more than the exposed K transfer of each later tile.
+// pays more than the exposed K transfer of each later tile.  For d > 64 each
+// lane fetches the residual of its epilogue elements together with Q, so that
+// the epilogue does not wait for HBM at the end of such short work-groups.
 #include "attn.h"
 #include "common.h"
 
@@ -102,6 +104,23 @@ sparse_wg_kernel(const AttnArgs a) {
         qf[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
     }
     const float rho_c = row_ok ? a.rho_in[(int64_t)bh * a.L + row] : 0.f;
+    // The residual of this lane's epilogue elements.  For d > 64 it is fetched here, so that its
+    // latency hides behind the tiles (the registers it holds leave the occupancy unchanged there);
+    // for d <= 64 the epilogue reads it, which keeps one more work-group per CU.
+    constexpr bool R_EARLY = DP >= 96;
+    u32x2 rreg[R_EARLY ? C::NDT : 1][4];
+    if constexpr (R_EARLY) {
+        const __amdgpu_buffer_rsrc_t rr =
+            __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)a.R_in + base), 0, nrec, 0x00020000);
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                const int d0 = 32 * dt + 8 * bb + 4 * h;
+                const uint32_t off = d0 < a.d ? (uint32_t)row * row_bytes + 2u * d0 : kOOB;
+                rreg[dt][bb] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rr, off, 0, 0));
+            }
+    }
 
     // 64-key tiles: tile t is part t % TPB of kept block t / TPB of this query block's CSR row
     const int e0 = scalar_load(rp, qb);
@@ -312,7 +331,9 @@ sparse_wg_kernel(const AttnArgs a) {
         for (int bb = 0; bb < 4; ++bb) {
             const int d0 = 32 * dt + 8 * bb + 4 * h;
             if (row_ok && d0 < a.d) {
-                const u32x2 rw = *(const u32x2*)(Rp + d0);
+                u32x2 rw;
+                if constexpr (R_EARLY) rw = rreg[dt][bb];
+                else rw = *(const u32x2*)(Rp + d0);
                 const int j = 4 * bb;
                 u32x2 ow;
                 ow[0] = pack_bf16(fmaf(scale, acc[dt][j], bf16_lo(rw[0])), fmaf(scale, acc[dt][j + 1], bf16_hi(rw[0])));
