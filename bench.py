@@ -23,6 +23,10 @@ After the timed steps (outside the timed region) the line also carries:
   workloads       calibration and sparse-step times of the other workloads
                   (the image workloads warm and after a 512 MiB cache flush;
                   the long-video workload at its four windows);
+  stream_floor    the time in which a plain streaming kernel (the in-tree probe
+                  `probe_stream`, non-temporal loads and stores, last-level cache
+                  evicted) moves the sparse step's traffic on the same device,
+                  and the sparse step's fraction of that rate;
   cpu_baseline    the CPU oracle's sparse step on the same workload, timed on
                   the host cores (float32 and float64 modes, a process pool over
                   (batch, head) slices with one BLAS thread per process).
@@ -32,6 +36,7 @@ usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -250,6 +255,23 @@ def extras(rt, c3_sets, rho_c3, r_c3):
     return out
 
 
+def stream_floor(sparse_ms, bytes_alg):
+    """The streaming probe's four-read/one-write mix (the sparse step's traffic, one 136.5 MB tensor per
+    stream), run as a child process after the timed region; its best time scaled to the step's
+    algorithmic bytes is the floor for moving them.  A missing or failing probe is reported, not fatal."""
+    exe = os.path.join(ROOT, "sparse_attention_diffusion_block_amd", "probe_stream")
+    if not os.path.exists(exe):
+        return {"error": "probe_stream is not built"}
+    try:
+        p = subprocess.run([exe, "--mix-json"], capture_output=True, text=True, timeout=120)
+        rec = json.loads(p.stdout.strip().splitlines()[-1])
+    except Exception as e:                      # noqa: BLE001 - reported in the line
+        return {"error": f"probe_stream: {e}"[:200]}
+    floor_ms = rec["best_us"] * 1e-3 * bytes_alg / rec["bytes"]
+    return {"probe": rec, "floor_ms": round(floor_ms, 4), "sparse_step_ms": round(sparse_ms, 4),
+            "sparse_frac_of_floor": round(floor_ms / sparse_ms, 4)}
+
+
 def copy_bandwidth():
     """Measured read + write rate of a plain 1 GiB device copy (the streaming ceiling of this chip)."""
     import torch
@@ -441,6 +463,8 @@ def main():
     }
     if not args.no_extras and args.config == 3:
         out.update(extras(rt, dev_sets, rho, r_cal))
+        log("extras: streaming floor (probe_stream)")
+        out["stream_floor"] = stream_floor(t_sp * 1e3, bytes_alg)
     if not args.no_cpu_baseline:
         rho_c, r_c = make_cache(B, H, L, d, seed=cfg.number, dtype=cfg.dtype)
         log("timing the CPU oracle (float32 and float64 modes)")

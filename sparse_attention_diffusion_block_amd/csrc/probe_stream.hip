@@ -10,10 +10,13 @@
 //            the sparse step (Q, K, V and R read, O written), sized like one of its tensors
 //            at B = 2, H = 30, L = 17776, d = 64 in bfloat16.
 // Before every timed launch a 4 GiB fill evicts the 256 MB last-level cache, so each sample reads
-// from HBM.  20 samples per row (HIP events around one launch); best and mean.
+// from HBM.  20 samples per row (HIP events around one launch); best and mean.  With --mix-json it
+// runs only the non-temporal mix (unrolled x1, 2 work-groups per CU) and prints one JSON line.
 #include <hip/hip_runtime.h>
 #include <stdio.h>
 #include <stdlib.h>
+
+#include <string>
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
@@ -89,7 +92,8 @@ __global__ void __launch_bounds__(256) mix_kernel(const u32x4* __restrict__ a, c
     for (; i < n; i += stride) o[i] = a[i] ^ b[i] ^ c[i] ^ d[i];
 }
 
-int main() {
+int main(int argc, char** argv) {
+    const bool mix_json = argc > 1 && std::string(argv[1]) == "--mix-json";
     const size_t bytes = (size_t)2 * 30 * 17776 * 64 * 2;   // one bfloat16 tensor of the video workload
     const size_t n = bytes / 16;
     const size_t big_bytes = (size_t)4 << 30;
@@ -111,9 +115,11 @@ int main() {
     CHECK(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
     hipDeviceProp_t prop;
     CHECK(hipGetDeviceProperties(&prop, dev));
-    printf("device: %s, %d CUs\n\n", prop.gcnArchName, cus);
-    printf("| pattern | policy | unroll | work-groups per CU | bytes moved | best us | best GB/s | mean us | mean GB/s |\n");
-    printf("|---|---|---|---|---|---|---|---|---|\n");
+    if (!mix_json) {
+        printf("device: %s, %d CUs\n\n", prop.gcnArchName, cus);
+        printf("| pattern | policy | unroll | work-groups per CU | bytes moved | best us | best GB/s | mean us | mean GB/s |\n");
+        printf("|---|---|---|---|---|---|---|---|---|\n");
+    }
 
     auto row = [&](const char* pattern, bool nt, int unroll, int per_cu, double moved, auto launch) {
         for (int w = 0; w < 3; ++w) launch();
@@ -132,9 +138,22 @@ int main() {
             total += ms;
         }
         const float mean = total / samples;
-        printf("| %s | %s | x%d | %d | %.0f | %.1f | %.0f | %.1f | %.0f |\n", pattern, nt ? "nt" : "default", unroll,
-               per_cu, moved, best * 1e3, moved / (best * 1e6), mean * 1e3, moved / (mean * 1e6));
+        if (mix_json)
+            printf("{\"pattern\": \"%s\", \"policy\": \"%s\", \"unroll\": %d, \"workgroups_per_cu\": %d, "
+                   "\"bytes\": %.0f, \"best_us\": %.1f, \"mean_us\": %.1f, \"best_gbs\": %.0f, \"samples\": %d}\n",
+                   pattern, nt ? "nt" : "default", unroll, per_cu, moved, best * 1e3, mean * 1e3, moved / (best * 1e6),
+                   samples);
+        else
+            printf("| %s | %s | x%d | %d | %.0f | %.1f | %.0f | %.1f | %.0f |\n", pattern, nt ? "nt" : "default", unroll,
+                   per_cu, moved, best * 1e3, moved / (best * 1e6), mean * 1e3, moved / (mean * 1e6));
     };
+    if (mix_json) {
+        const dim3 grid(cus * 2), blk(256);
+        row("mix 4R+1W", true, 1, 2, 5.0 * bytes,
+            [&] { hipLaunchKernelGGL((mix_kernel<1, true>), grid, blk, 0, 0, a, b, c, d, o, n); });
+        CHECK(hipGetLastError());
+        return 0;
+    }
 
     for (int per_cu : {2, 4, 8}) {
         const dim3 grid(cus * per_cu), blk(256);
