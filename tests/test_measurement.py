@@ -80,3 +80,30 @@ def test_roofline_bound_and_fraction():
     r = measure._roofline(4.08e13, 3.55e9, 42.4e-3)
     assert r["bound"] == "mfma" and r["attainable_tflops"] == pytest.approx(measure.MFMA_PEAK_TFLOPS, abs=0.05)
     assert r["roofline_frac"] == pytest.approx(4.08e13 / 42.4e-3 / peak_flops, abs=1e-4)
+
+
+def test_stream_floor_scales_the_probe_to_the_step(monkeypatch, tmp_path):
+    """The floor is the probe's best time scaled to the step's algorithmic bytes; a probe that is
+    missing or prints nothing usable is reported in the line, not raised."""
+    import json
+    import subprocess
+    exe = tmp_path / "sparse_attention_diffusion_block_amd" / "probe_stream"
+    exe.parent.mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert "error" in bench.stream_floor(0.2, 686_864_640)             # not built
+    exe.write_text("")
+    rec = {"pattern": "mix 4R+1W", "policy": "nt", "bytes": 682598400, "best_us": 120.0, "mean_us": 122.0}
+
+    class Done:
+        stdout = "warm-up line\n" + json.dumps(rec) + "\n"
+    monkeypatch.setattr(subprocess, "run", lambda *a, **k: Done())
+    out = bench.stream_floor(0.24, 686_864_640)
+    floor = 0.120 * 686_864_640 / 682598400
+    assert out["floor_ms"] == pytest.approx(floor, abs=1e-4)
+    assert out["sparse_frac_of_floor"] == pytest.approx(floor / 0.24, abs=1e-4)
+    assert out["probe"]["policy"] == "nt"
+
+    class Garbled:
+        stdout = "not json\n"
+    monkeypatch.setattr(subprocess, "run", lambda *a, **k: Garbled())
+    assert "error" in bench.stream_floor(0.24, 686_864_640)
