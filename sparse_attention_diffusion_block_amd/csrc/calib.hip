@@ -203,6 +203,8 @@ __global__ void __launch_bounds__(CalCfg<DP>::NT, CalCfg<DP>::WPS) calib_kernel(
     float mref = -INFINITY, d_in = 0.f, d_out = 0.f;
 
     const int swn = swz(n);
+    // d within the first DP - 16 elements: the last 16-element k-step of S^T holds only zeros
+    const bool short_d = __builtin_amdgcn_readfirstlane(a.d) <= DP - 16;
     const int s16 = lane & 15, g = lane >> 4;
     const int fv = ((s16 >> 2) << 1) | h;
     const int vrow = (4 * h + (s16 >> 2)) * C::RS;
@@ -225,10 +227,12 @@ __global__ void __launch_bounds__(CalCfg<DP>::NT, CalCfg<DP>::WPS) calib_kernel(
         if constexpr (C::QLDS) asm volatile("" : "+v"(qoff));   // re-read Q every tile, not kept in registers
 
         // S^T for the tile's two 32-key halves: two independent MFMA chains, issued alternately
+        // (the last k-step is skipped when it covers only padding: d = 72 at DP = 96)
         f32x16 sacc[2];
         sacc[0] = sacc[1] = f32x16{};
 #pragma unroll
         for (int s = 0; s < C::NS; ++s) {
+            if (s == C::NS - 1 && short_d) break;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
                 const uint16_t* kr = ks + (kt * 32 + n) * C::RS;
