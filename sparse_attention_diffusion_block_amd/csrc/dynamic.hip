@@ -11,7 +11,9 @@
 // Two launches:
 //   dyn_pool_kernel  one work-group per (block, slice) reads the block's Q and
 //                    K rows once (16-byte loads) and writes both means (fp32);
-//                    the whole pass is one read of Q and K: HBM-bound.
+//                    the whole pass is one read of Q and K: HBM-bound.  The
+//                    rows are read whole and never again, so the loads carry the
+//                    non-temporal hint (cold, about twice the default rate);
 //   dyn_topk_kernel  one wave per R query blocks: lane j scores key blocks
 //                    j, j + 64, ... against the key means staged 64 at a time
 //                    in LDS (each staged tile serves the work-group's 4 R
@@ -46,8 +48,8 @@ __global__ void __launch_bounds__(256) dyn_pool_kernel(const void* __restrict__ 
         for (int r = r0; r < nrows; r += rp) {
             const int64_t off = base + (int64_t)(row0 + r) * sl + c * EPC;
             if constexpr (BF16) {
-                const u32x4 wq = *(const u32x4*)((const uint16_t*)Q + off);
-                const u32x4 wk = *(const u32x4*)((const uint16_t*)K + off);
+                const u32x4 wq = __builtin_nontemporal_load((const u32x4*)((const uint16_t*)Q + off));
+                const u32x4 wk = __builtin_nontemporal_load((const u32x4*)((const uint16_t*)K + off));
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     sq[2 * i] += bf16_lo(wq[i]);
@@ -56,8 +58,8 @@ __global__ void __launch_bounds__(256) dyn_pool_kernel(const void* __restrict__ 
                     sk[2 * i + 1] += bf16_hi(wk[i]);
                 }
             } else {
-                const f32x4 wq = *(const f32x4*)((const float*)Q + off);
-                const f32x4 wk = *(const f32x4*)((const float*)K + off);
+                const f32x4 wq = __builtin_nontemporal_load((const f32x4*)((const float*)Q + off));
+                const f32x4 wk = __builtin_nontemporal_load((const f32x4*)((const float*)K + off));
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     sq[i] += wq[i];

@@ -3,7 +3,7 @@
     python -m sparse_attention_diffusion_block_amd.measure sweep    [--runs 50]
     python -m sparse_attention_diffusion_block_amd.measure configs  [--runs 50]
     python -m sparse_attention_diffusion_block_amd.measure peaks
-    python -m sparse_attention_diffusion_block_amd.measure dynamic  [--runs 50] [--keep 9]
+    python -m sparse_attention_diffusion_block_amd.measure dynamic  [--runs 50] [--keep 9] [--cache both]
     python -m sparse_attention_diffusion_block_amd.measure graph    [--runs 50]
     python -m sparse_attention_diffusion_block_amd.measure kernels  --config N [--runs 3] [--mask I]
 
@@ -15,7 +15,7 @@ configs  calibration and sparse-step times of every workload and mask; the two i
          workloads, whose working sets fit in the 256 MB last-level cache, are also
          timed cold (after writing a 512 MiB buffer before each run).
 dynamic  on the CogVideoX-2B-like shapes: the dynamic block-mask index (block means of Q
-         and K, then a per-row top-keep; one read of Q and K, so HBM-bound), and the sparse
+         and K, then a per-row top-keep; one read of Q and K, so HBM-bound; warm and cold), and the sparse
          step on that per-(batch, head) index beside the static mask shared by all heads
          and the same static mask given once per head.
 graph    wall time of one refresh period (a calibration and the sparse steps until the next
@@ -186,12 +186,20 @@ def cmd_dynamic(args):
     nb = -(-cfg.L // cfg.block)
     ws = torch.empty(rt.dynamic_workspace_bytes(q, cfg.block), dtype=torch.uint8, device="cuda")
     dyn = rt.dynamic_index(q, k, args.keep, cfg.block, workspace=ws)
-    t = _time(lambda: rt.dynamic_index(q, k, args.keep, cfg.block, workspace=ws, out=dyn), args.runs)
     nbytes = 2 * cfg.B * cfg.H * cfg.L * cfg.d * 2     # one read of Q and K
-    s_ = t["median_ms"] * 1e-3
-    print(json.dumps({"what": "dynamic_index", "workload": cfg.name, "keep": args.keep, **t,
-                      "algorithmic_gbs": round(nbytes / s_ / 1e9, 1),
-                      "hbm_frac": round(nbytes / s_ / 1e9 / HBM_PEAK_GBS, 4)}), flush=True)
+    # warm: back to back on one input (Q and K, 273 MB, partly stay in the 256 MB last-level cache);
+    # cold: a 512 MiB write before every call, so Q and K come from HBM
+    flush = torch.empty(512 << 18, dtype=torch.float32, device="cuda")
+    for label, before in (("warm", None), ("cold", lambda: flush.zero_())):
+        if args.cache not in (label, "both"):
+            continue
+        t = _time(lambda: rt.dynamic_index(q, k, args.keep, cfg.block, workspace=ws, out=dyn), args.runs,
+                  before=before)
+        s_ = t["median_ms"] * 1e-3
+        print(json.dumps({"what": "dynamic_index", "workload": cfg.name, "keep": args.keep, "cache": label, **t,
+                          "algorithmic_gbs": round(nbytes / s_ / 1e9, 1),
+                          "hbm_frac": round(nbytes / s_ / 1e9 / HBM_PEAK_GBS, 4)}), flush=True)
+    del flush
     static = rt.mask_build(spec.kind, spec.nb, spec.w, spec.text_blocks, spec.tshift)
     per_head = rt.index_build(np.broadcast_to(static, (cfg.H, nb, nb)).copy(), cfg.block)
     masks = {"static (shared)": (rt.index_build(static, cfg.block), static[None]),
@@ -312,6 +320,8 @@ def main(argv=None):
             sp.add_argument("--mask", type=int, default=None, help="only this mask of the workload (0-based)")
         if name == "dynamic":
             sp.add_argument("--keep", type=int, default=9)
+            sp.add_argument("--cache", choices=("warm", "cold", "both"), default="both",
+                            help="time the index back to back (warm), after a cache flush (cold), or both")
     args = ap.parse_args(argv)
     import torch
     if not torch.cuda.is_available():
