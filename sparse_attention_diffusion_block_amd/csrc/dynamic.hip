@@ -92,15 +92,16 @@ template <int MM, int R, int DP>
 __global__ void __launch_bounds__(256) dyn_topk_kernel(const float* __restrict__ qm, const float* __restrict__ km,
                                                        int nb, int d, int kk, uint8_t* __restrict__ mask,
                                                        int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx) {
-    // the work-group's 4 R query means (row stride DP), then 64 key means (row stride DP + 1: the
-    // lanes' reads of one column fall in distinct banks)
+    // the work-group's 4 R query means (row stride DP), then 64 key means (row stride DP + 4: each
+    // lane reads four columns of its own row with one 16-byte read, and 16 lanes' reads fall in
+    // distinct banks)
     __shared__ __attribute__((aligned(16))) float qs[4 * R * DP];
-    __shared__ float kt[64 * (DP + 1)];
+    __shared__ __attribute__((aligned(16))) float kt[64 * (DP + 4)];
     const int s = blockIdx.y;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int q0 = blockIdx.x * 4 * R;     // the work-group's first query block
     const int a0 = q0 + wave * R;          // this wave's first query block
-    constexpr int ldk = DP + 1;
+    constexpr int ldk = DP + 4;
     const float* qms = qm + (int64_t)s * nb * d;
     const float* kms = km + (int64_t)s * nb * d;
     for (int e = threadIdx.x; e < 4 * R * DP; e += 256) {
@@ -134,11 +135,7 @@ __global__ void __launch_bounds__(256) dyn_topk_kernel(const float* __restrict__
             for (int i = 0; i < TC; ++i) {
                 const int rr = r0 + i * rpp;
                 if (r0 < rpp && rr < 64) {
-                    float* dst = kt + rr * ldk + 4 * c4;
-                    dst[0] = pre[i][0];
-                    dst[1] = pre[i][1];
-                    dst[2] = pre[i][2];
-                    dst[3] = pre[i][3];
+                    *(f32x4*)(kt + rr * ldk + 4 * c4) = pre[i];
                 }
             }
             __syncthreads();
@@ -150,7 +147,8 @@ __global__ void __launch_bounds__(256) dyn_topk_kernel(const float* __restrict__
             for (int r = 0; r < R; ++r) acc[r] = 0.f;
 #pragma unroll
             for (int cc = 0; cc < DP; cc += 4) {
-                const float k0 = kr[cc], k1 = kr[cc + 1], k2 = kr[cc + 2], k3 = kr[cc + 3];
+                const f32x4 kv = *(const f32x4*)(kr + cc);
+                const float k0 = kv[0], k1 = kv[1], k2 = kv[2], k3 = kv[3];
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     const f32x4 qv = *(const f32x4*)(qr + r * DP + cc);
