@@ -89,6 +89,12 @@ SMALL = [
     ("bf16-b64-d96-emptyrow-tail", "bf16", 2, 1, 300, 96, 64,
      lambda nb: random_mask(nb, nb, 0.5, 16, empty_rows=(1,))),
     ("bf16-b64-d112-band-tail", "bf16", 1, 2, 460, 112, 64, lambda nb: om.band_mask(nb, 3)),
+    # head dims whose last 16-element k-step of S^T is all padding (d <= DP - 16), which the
+    # calibration skips: d = 16 at DP 32, d = 80 at DP 96 with 64- and 128-token blocks
+    ("bf16-b64-d16-band-tail", "bf16", 1, 2, 300, 16, 64, lambda nb: om.band_mask(nb, 2)),
+    ("bf16-b64-d80-rand-emptyrow", "bf16", 2, 1, 330, 80, 64,
+     lambda nb: random_mask(nb, nb, 0.5, 17, empty_rows=(2,))),
+    ("bf16-b128-d80-cog-tail", "bf16", 1, 2, 420, 80, 128, lambda nb: om.cogvideo3d_mask(nb, 1, 2)),
 ]
 
 
